@@ -1,0 +1,231 @@
+"""Python binding of libgdn.so, the MI355X Gated DeltaNet engine.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gdn.h``.  Torch supplies device
+memory and the current HIP stream.  There is no fallback: if the library is
+missing or fails to load, importing the entry points raises.
+
+Entry points (same names as the C ABI):
+
+``gdn_prefill_chunked``       chunked prefill with explicit initial/final state
+``gdn_recurrent_step``        token-by-token step with compact state-update capture
+``gdn_replay_state_updates``  replay of captured (decay, key, delta) records
+``gdn_state_snapshot``        immutable copy of a state set
+``gdn_prefill_workspace_bytes``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+_DTYPES = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
+EXPORTED = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+            "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot",
+            "gdn_status_string", "gdn_last_error")
+
+
+class gdn_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hv", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdn.so (once).  Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m gated_deltanet_03_amd._build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    shp = ctypes.POINTER(gdn_shape)
+    lib.gdn_abi_version.restype = i32
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_prefill_workspace_bytes.restype = sz
+    lib.gdn_prefill_workspace_bytes.argtypes = [shp, i32, i32]
+    lib.gdn_prefill_chunked.restype = i32
+    lib.gdn_prefill_chunked.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]
+    lib.gdn_recurrent_step.restype = i32
+    lib.gdn_recurrent_step.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, i32, vp, vp]
+    lib.gdn_replay_state_updates.restype = i32
+    lib.gdn_replay_state_updates.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.gdn_state_snapshot.restype = i32
+    lib.gdn_state_snapshot.argtypes = [vp, vp, i64, i32, i32, i32, vp]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [i32]
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != GDN_OK:
+        lib = load_library()
+        raise GdnError(status, f"{lib.gdn_status_string(status).decode()}: {lib.gdn_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    if device is None or device.type != "cuda":
+        return ctypes.c_void_p(0)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _shape_from(q, k, v, scale, cu_seqlens):
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense q must be [B, T, Hq, dk]")
+        B, T, Hq, dk = q.shape
+    else:
+        if q.dim() == 4:
+            if q.shape[0] != 1:
+                raise ValueError("ragged q must be [1, T, Hq, dk] or [T, Hq, dk]")
+            q = q[0]
+        T, Hq, dk = q.shape
+        B = cu_seqlens.numel() - 1
+    Hv, dv = v.shape[-2], v.shape[-1]
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if scale is None:
+        scale = dk ** -0.5
+    return gdn_shape(B, T, Hq, Hv, dk, dv, float(scale), _DTYPES[q.dtype])
+
+
+def gdn_prefill_workspace_bytes(shape: gdn_shape, chunk_size: int, ragged: bool) -> int:
+    return int(load_library().gdn_prefill_workspace_bytes(ctypes.byref(shape), chunk_size, int(bool(ragged))))
+
+
+def gdn_prefill_chunked(q, k, v, g, beta, *, scale=None, initial_state=None,
+                        initial_state_batch_stride=None, cu_seqlens=None, chunk_size=64,
+                        o=None, final_state=None, output_final_state=True, workspace=None):
+    """Chunked prefill.  Dense q/k [B,T,Hq,dk], v [B,T,Hv,dv], g/beta [B,T,Hv];
+    ragged: the same without B (or B=1) plus cu_seqlens int32 [N+1] on the device.
+    Returns (o, final_state or None)."""
+    lib = load_library()
+    dev = q.device
+    sh = _shape_from(q, k, v, scale, cu_seqlens)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(initial_state, "initial_state", torch.float32, dev)
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, dev)
+    per = sh.Hv * sh.dk * sh.dv
+    if final_state is None and output_final_state:
+        final_state = torch.empty((sh.B, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev)
+    if initial_state_batch_stride is None:
+        initial_state_batch_stride = 0 if (initial_state is not None and initial_state.shape[0] == 1
+                                           and sh.B > 1) else per
+    need = gdn_prefill_workspace_bytes(sh, chunk_size, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib.gdn_prefill_chunked(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(initial_state), int(initial_state_batch_stride), _ptr(cu_seqlens),
+                                   int(chunk_size), _ptr(o), _ptr(final_state), _ptr(workspace),
+                                   workspace.numel(), _stream(dev)))
+    return o, final_state
+
+
+def gdn_recurrent_step(q, k, v, g, beta, *, scale=None, initial_state=None,
+                       initial_state_batch_stride=None, cu_seqlens=None, o=None, final_state=None,
+                       output_final_state=True, state_update_capacity=0, capture_count=None,
+                       state_update_active=1, state_update=None):
+    """Recurrent step with optional compact capture.  Returns (o, final_state, state_update)."""
+    lib = load_library()
+    dev = q.device
+    sh = _shape_from(q, k, v, scale, cu_seqlens)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(initial_state, "initial_state", torch.float32, dev)
+    _need(capture_count, "capture_count", torch.int32, dev)
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, dev)
+    per = sh.Hv * sh.dk * sh.dv
+    if final_state is None and output_final_state:
+        final_state = torch.empty((sh.B, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev)
+    if initial_state_batch_stride is None:
+        initial_state_batch_stride = 0 if (initial_state is not None and initial_state.shape[0] == 1
+                                           and sh.B > 1) else per
+    cap = int(state_update_capacity)
+    if cap > 0 and state_update is None:
+        R = sh.Hv + sh.Hq * sh.dk + sh.Hv * sh.dv
+        state_update = torch.empty((sh.B, cap, R), dtype=torch.float32, device=dev)
+    _need(state_update, "state_update", torch.float32, dev)
+    _check(lib.gdn_recurrent_step(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), int(initial_state_batch_stride), _ptr(cu_seqlens),
+                                  _ptr(o), _ptr(final_state), cap, _ptr(capture_count),
+                                  int(state_update_active), _ptr(state_update), _stream(dev)))
+    return o, final_state, state_update
+
+
+def gdn_replay_state_updates(state, state_update, replay_count, *, Hq, state_update_capacity=None):
+    """Replay the first replay_count[b] records of each row onto state (in place)."""
+    lib = load_library()
+    dev = state.device
+    B, Hv, dk, dv = state.shape
+    cap = state_update.shape[1] if state_update_capacity is None else int(state_update_capacity)
+    _need(state, "state", torch.float32, dev)
+    _need(state_update, "state_update", torch.float32, dev)
+    _need(replay_count, "replay_count", torch.int32, dev)
+    _check(lib.gdn_replay_state_updates(B, int(Hq), Hv, dk, dv, cap, _ptr(state_update), _ptr(replay_count),
+                                        _ptr(state), _stream(dev)))
+    return state
+
+
+def gdn_state_snapshot(src, dst=None):
+    """Bitwise copy of a [N, Hv, dk, dv] fp32 state set, ordered on the current stream."""
+    lib = load_library()
+    dev = src.device
+    _need(src, "src", torch.float32, dev)
+    if dst is None:
+        dst = torch.empty_like(src)
+    _need(dst, "dst", torch.float32, dev)
+    N, Hv, dk, dv = src.shape
+    _check(lib.gdn_state_snapshot(_ptr(src), _ptr(dst), N, Hv, dk, dv, _stream(dev)))
+    return dst
+
+
+__all__ = ["load_library", "GdnError", "gdn_shape", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+           "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot", "EXPORTED", "LIB_PATH"]

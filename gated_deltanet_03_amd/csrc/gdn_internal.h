@@ -1,0 +1,77 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Recurrent step (token-by-token) problem, already validated on the host.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* s0;       // may be null (zeros)
+  int64_t s0_stride;     // elements between sequences' initial states (0 = broadcast)
+  float* s_out;          // may be null
+  void* o;
+  const int32_t* cu;     // null = dense rows
+  int32_t B, T, total;   // rows, tokens per row (dense), total packed tokens
+  int32_t Hq, Hv, dk, dv;
+  float scale;
+  int32_t cap;           // capture capacity (0 = no capture)
+  const int32_t* counts; // [B] capture counts (device)
+  int32_t active;
+  float* su;             // [B, cap, R]
+};
+
+struct ReplayArgs {
+  int32_t B, Hq, Hv, dk, dv, cap;
+  const float* su;
+  const int32_t* counts;
+  float* state;
+};
+
+// Chunked prefill problem.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* s0;
+  int64_t s0_stride;
+  float* s_out;
+  void* o;
+  const int32_t* cu;
+  int32_t B, T, total;   // total = packed tokens
+  int32_t Hq, Hv, dk, dv;
+  float scale;
+  int32_t chunk;         // 16, 32 or 64
+  int32_t max_chunks;    // workspace capacity in chunks
+  int32_t* chunk_offsets;   // [B+1] inside the workspace
+  void* chunk_data;         // per (chunk, value head) blocks inside the workspace
+};
+
+// Per (chunk, value head) workspace block written by the chunk-prep kernel:
+//   A'  [64][64] element type (the UT inverse times diag(beta))
+//   MP  [64][64] element type (decay-masked Q K^T, lower triangle incl. diag)
+//   gam [64] fp32 (exp of the in-chunk cumulative log decay)
+//   tail[64] fp32 (exp(G_last - G_i), decay from token i to the chunk end)
+inline size_t chunk_block_bytes(DType dt) {
+  size_t es = dt == DType::F32 ? 4 : 2;
+  return 64 * 64 * es * 2 + 64 * 4 * 2;
+}
+
+hipError_t launch_recurrent(DType dt, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_zero_fill(float* p, size_t n, hipStream_t s);
+hipError_t launch_replay(const ReplayArgs& a, hipStream_t s);
+hipError_t launch_copy(const float* src, float* dst, size_t n, hipStream_t s);
+hipError_t launch_prefill(DType dt, const PrefillArgs& a, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,162 @@
+"""GPU parity of the chunked prefill against the fp64 token-by-token oracle.
+
+Small cases are compared in full; the full-size workloads (2048-token fp16,
+14286-token packed bf16, the 4096-token prefix plus batches) are compared on
+sampled value heads, which the oracle computes one by one.
+"""
+
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+from gpu_common import DEV, assert_close, say, sha, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_03_amd as m
+    m.load_library()
+    return m
+
+
+def prefill(gdn, case, chunk, heads_out=True, **kw):
+    d = to_dev(case)
+    if d["cu_seqlens"] is None:
+        B = case["num_seqs"]
+        args = [d[x].reshape(B, -1, *d[x].shape[1:]) for x in ("q", "k", "v", "g", "beta")]
+    else:
+        args = [d[x] for x in ("q", "k", "v", "g", "beta")]
+    kw.setdefault("initial_state", d["s0"])
+    o, fin = gdn.gdn_prefill_chunked(*args, scale=case["scale"], cu_seqlens=d["cu_seqlens"], chunk_size=chunk,
+                                     **kw)
+    torch.cuda.synchronize()
+    return o.reshape(-1, case["Hv"], case["dv"]), fin
+
+
+def oracle_run(case, heads=None, s0="case", broadcast=False):
+    return oracle.recurrent(case["q"], case["k"], case["v"], case["g"], case["beta"], case["scale"],
+                            case["Hq"], case["Hv"], cu_seqlens=case["cu_seqlens"], num_seqs=case["num_seqs"],
+                            initial_state=case["s0"] if isinstance(s0, str) else s0, heads=heads,
+                            initial_state_broadcast=broadcast)
+
+
+def test_prefill_tiny_fp32_chunk16(gdn):
+    case = gi.make("tiny_fp32")
+    say(f"case tiny_fp32 prefill chunk 16 seed={case['seed']}")
+    o, fin = prefill(gdn, case, case["chunk"])
+    ref = oracle_run(case)
+    assert_close(o, ref["o"], "f32", "o")
+    assert_close(fin, ref["final"], "f32", "final")
+    # chunked equals recurrent on the device too
+    d = to_dev(case)
+    o_r, fin_r, _ = gdn.gdn_recurrent_step(*[d[x].reshape(1, 64, *d[x].shape[1:]) for x in
+                                             ("q", "k", "v", "g", "beta")], scale=case["scale"])
+    assert_close(o, o_r.reshape(-1, 1, 16), "f32", "chunked vs recurrent o")
+    assert_close(fin, fin_r, "f32", "chunked vs recurrent final")
+
+
+def test_prefill_qwen_fp16(gdn):
+    case = gi.make("qwen_fp16")
+    say(f"case qwen_fp16 T=2048 Hq=2 Hv=6 seed={case['seed']}")
+    o, fin = prefill(gdn, case, case["chunk"])
+    ref = oracle_run(case)
+    assert_close(o, ref["o"], "f16", "o")
+    assert_close(fin, ref["final"], "f16", "final")
+
+
+def test_prefill_long_varlen_sampled_heads(gdn):
+    case = gi.make("long_varlen")
+    say(f"case long_varlen lengths={case['lengths']} seed={case['seed']}")
+    o, fin = prefill(gdn, case, case["chunk"])
+    heads = [0, 17, 31]   # key heads 0 and 8 (two value heads of key head 0 differ by decay only)
+    ref = oracle_run(case, heads=heads)
+    for h in heads:
+        for s, (t0, t1) in enumerate(oracle.sequence_bounds(0, 0, case["cu_seqlens"].numpy())):
+            assert_close(o[t0:t1, h], ref["o"][t0:t1, h], "bf16", f"o seq {s} head {h}")
+            assert_close(fin[s, h], ref["final"][s, h], "bf16", f"final seq {s} head {h}")
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_prefill_ragged_chunk_boundaries(gdn, chunk, dtype):
+    lengths = [0, 1, 15, 16, 17, 63, 64, 65, 130]
+    case = gi.random_case(500 + chunk, lengths, Hq=2, Hv=4, dk=64, dv=128, dtype=dtype)
+    say(f"case ragged {dtype} chunk={chunk} lengths={lengths}")
+    o, fin = prefill(gdn, case, chunk)
+    ref = oracle_run(case)
+    assert_close(o, ref["o"], dtype, "o")
+    assert_close(fin, ref["final"], dtype, "final")
+    assert torch.equal(fin[0].cpu(), case["s0"][0])        # empty sequence: final = initial
+
+
+@pytest.mark.parametrize("dk,dv,Hq,Hv", [(16, 16, 1, 1), (32, 64, 2, 2), (128, 32, 1, 4), (64, 16, 3, 6)])
+def test_prefill_head_dims(gdn, dk, dv, Hq, Hv):
+    case = gi.random_case(600 + dk + dv, [70, 33], Hq=Hq, Hv=Hv, dk=dk, dv=dv, dtype="bf16")
+    say(f"case head dims dk={dk} dv={dv} Hq={Hq} Hv={Hv}")
+    o, fin = prefill(gdn, case, 64)
+    ref = oracle_run(case)
+    assert_close(o, ref["o"], "bf16", "o")
+    assert_close(fin, ref["final"], "bf16", "final")
+
+
+def test_prefill_chunk_size_does_not_change_results(gdn):
+    case = gi.random_case(700, [200, 77], Hq=2, Hv=4, dk=128, dv=128, dtype="bf16")
+    say("case chunk-size independence")
+    outs = [prefill(gdn, case, c) for c in (16, 32, 64)]
+    for o, fin in outs[1:]:
+        assert_close(o, outs[0][0], "bf16", "o across chunk sizes")
+        assert_close(fin, outs[0][1], "bf16", "final across chunk sizes")
+
+
+def test_prefill_split_sequence_carries_state(gdn):
+    """Prefill [0, m) then [m, T) from the carried final state equals [0, T)."""
+    case = gi.random_case(710, [300], Hq=2, Hv=4, dk=128, dv=128, dtype="bf16")
+    say("case split prefill carry")
+    o_all, fin_all = prefill(gdn, case, 64)
+    m = 100
+    first = dict(case, q=case["q"][:m], k=case["k"][:m], v=case["v"][:m], g=case["g"][:m],
+                 beta=case["beta"][:m], cu_seqlens=torch.tensor([0, m], dtype=torch.int32), T=m)
+    second = dict(case, q=case["q"][m:], k=case["k"][m:], v=case["v"][m:], g=case["g"][m:],
+                  beta=case["beta"][m:], cu_seqlens=torch.tensor([0, 300 - m], dtype=torch.int32), T=300 - m)
+    o1, f1 = prefill(gdn, first, 64)
+    o2, f2 = prefill(gdn, second, 64, initial_state=f1)
+    assert_close(torch.cat([o1, o2]), o_all, "bf16", "o split vs whole")
+    assert_close(f2, fin_all, "bf16", "final split vs whole")
+
+
+def test_prefill_in_place_final_state(gdn):
+    case = gi.random_case(720, [90, 40], Hq=2, Hv=4, dk=128, dv=128, dtype="bf16")
+    say("case in-place final state")
+    o1, fin1 = prefill(gdn, case, 64)
+    st = case["s0"].to(DEV).clone()
+    o2, fin2 = prefill(gdn, case, 64, initial_state=st, final_state=st)
+    assert torch.equal(o1, o2) and torch.equal(fin1, st)
+
+
+def test_prefix_snapshot_reuse(gdn):
+    """Prefill a 4096-token prefix, snapshot it, run batches of 16 x 256 branching
+    from the snapshot (stride-0 broadcast); the snapshot stays bit-identical and
+    sampled outputs match the oracle continuing from its own prefix state."""
+    pre = gi.make("prefix_reuse", part="prefix")
+    say(f"case prefix_reuse prefix seed={pre['seed']}")
+    _, pfin = prefill(gdn, pre, 64)
+    snap = gdn.gdn_state_snapshot(pfin)
+    torch.cuda.synchronize()
+    h0 = sha(snap)
+    heads = [5, 26]
+    pref = oracle_run(pre, heads=heads)
+    checked = {0, 3}
+    for bi in range(8):
+        bt = gi.make("prefix_reuse", part="batch", batch_index=bi)
+        o, fin = prefill(gdn, bt, 64, initial_state=snap, initial_state_batch_stride=0,
+                         output_final_state=False)
+        assert sha(snap) == h0, f"snapshot changed after batch {bi}"
+        if bi in checked:
+            say(f"oracle check batch {bi}")
+            ref = oracle_run(bt, heads=heads, s0=pref["final"][:1], broadcast=True)
+            for h in heads:
+                assert_close(o[:, h], ref["o"][:, h], "bf16", f"batch {bi} head {h}")
