@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN hot path on one MI355X.
+
+One step = one pass over every stage of the hot path on one batch of synthetic
+input, all inputs resident in HBM before timing starts:
+
+  1. gdn_prefill_chunked      4 packed bf16 sequences of 8192/5000/1031/63 tokens,
+                              Hq=16, Hv=32, dk=dv=128, chunk 64, per-sequence
+                              initial states, final states written
+  2. gdn_state_snapshot       of those 4 final states
+  3. gdn_recurrent_step       8 ragged rows of <= 7 bf16 tokens (Hq=16, Hv=32,
+                              dk=dv=128) with compact capture (capacity 7)
+  4. gdn_replay_state_updates every captured record onto the pre-step states
+
+Prefill inputs rotate over 2 copies and decode/replay states over 48 distinct
+16 MB state sets so the 256 MB Infinity Cache cannot hold a step's data.
+Timing: torch.cuda events around the K timed steps (our kernels run on torch's
+current stream) and, per kernel, the library's own HIP-event pairs recorded on
+the launch stream over the same timed region.  Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s (MFMA % of peak); decode/replay state GB/s (% of HBM peak)"
+PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak
+PEAK_HBM_GBS = 8000.0               # MI355X HBM3E
+STATE_SETS = 48
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- #
+# algorithmic work
+# ----------------------------------------------------------------------------- #
+def chunk_sizes(lengths, C):
+    out = []
+    for L in lengths:
+        out += [C] * (L // C) + ([L % C] if L % C else [])
+    return out
+
+
+def prefill_flops(lengths, C, Hq, Hv, dk, dv):
+    """GEMM flops of the chunked method (dense counts, triangular solve excluded)."""
+    return sum(Hq * 4 * c * c * dk + Hv * (2 * c * c * dk + 4 * c * c * dv + 6 * c * dk * dv)
+               for c in chunk_sizes(lengths, C))
+
+
+def state_kernel_flops(lengths, C, Hv, dk, dv):
+    """Flops the sequential state pass performs: K S, Q S, K^T Delta (6 c dk dv) and
+    A' X, MP Delta (4 c^2 dv), per chunk per value head (dense counts)."""
+    return sum(Hv * (6 * c * dk * dv + 4 * c * c * dv) for c in chunk_sizes(lengths, C))
+
+
+def prep_kernel_flops(lengths, C, Hq, dk):
+    """Gram products K K^T and Q K^T per chunk per key head (the inverse is excluded)."""
+    return sum(Hq * 4 * c * c * dk for c in chunk_sizes(lengths, C))
+
+
+def prefill_bytes(T, N, Hq, Hv, dk, dv, es):
+    return T * (2 * Hq * dk * es + 2 * Hv * dv * es + 8 * Hv) + 2 * N * Hv * dk * dv * 4
+
+
+def decode_bytes(lengths, counts, cap, Hq, Hv, dk, dv, es):
+    R = Hv + Hq * dk + Hv * dv
+    toks = sum(lengths)
+    n = [min(max(c, 0), cap, L) for c, L in zip(counts, lengths)]
+    state = len(lengths) * Hv * dk * dv * 4 * 2
+    io = toks * (2 * Hq * dk * es + 2 * Hv * dv * es + 8 * Hv)
+    return state + io + sum(n) * R * 4, n
+
+
+def replay_bytes(m, Hq, Hv, dk, dv):
+    R = Hv + Hq * dk + Hv * dv
+    rows = sum(1 for x in m if x > 0)
+    return rows * Hv * dk * dv * 4 * 2 + sum(m) * R * 4
+
+
+# ----------------------------------------------------------------------------- #
+# traffic from committed rocprofv3 counter summaries
+# ----------------------------------------------------------------------------- #
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("gdn_prefill.hip", "gdn_recurrent.hip", "gdn_mfma.h", "gdn_device.h", "gdn_internal.h"):
+        with open(os.path.join(ROOT, "gated_deltanet_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel):
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != kernel_source_sha():
+        return None          # counters were taken on another version of the kernels
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- #
+# CPU baseline: the fp64 oracle on a bounded sample of the same step
+# ----------------------------------------------------------------------------- #
+def cpu_baseline(pre, dec, budget_s):
+    import oracle
+    threads = 1
+    t0 = time.perf_counter()
+    od = oracle.recurrent(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], dec["scale"], dec["Hq"], dec["Hv"],
+                          cu_seqlens=dec["cu_seqlens"], initial_state=dec["s0"])
+    buf, _ = oracle.capture(dec["k"], od["alpha"], od["delta"], dec["Hq"], dec["Hv"], dec["capacity"],
+                            dec["capture_count"].numpy(), 1, cu_seqlens=dec["cu_seqlens"])
+    n = [min(max(int(c), 0), dec["capacity"], L) for c, L in zip(dec["capture_count"].tolist(), dec["lengths"])]
+    oracle.replay(dec["s0"], buf, n, dec["Hq"], dec["Hv"], dec["dk"], dec["dv"], dec["capacity"])
+    t_dec = time.perf_counter() - t0
+    # prefill: whole packed workload, a subset of value heads (each head is independent)
+    heads, t_pre = [], 0.0
+    order = [0, 31, 8, 23, 16, 5, 27, 12, 19, 2, 29, 10, 21, 14, 25, 6]
+    for h in order:
+        t1 = time.perf_counter()
+        oracle.recurrent(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], pre["scale"], pre["Hq"], pre["Hv"],
+                         cu_seqlens=pre["cu_seqlens"], initial_state=pre["s0"], heads=[h])
+        t_pre += time.perf_counter() - t1
+        heads.append(h)
+        if t_pre + t_dec > budget_s:
+            break
+    est_step = t_pre * pre["Hv"] / len(heads) + t_dec
+    tokens = pre["T"] + dec["T"]
+    return {"value": tokens / est_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, single thread: the full decode+capture+replay stage "
+                       f"({t_dec:.2f} s) and the full {pre['T']}-token prefill for {len(heads)} of "
+                       f"{pre['Hv']} value heads ({t_pre:.2f} s), scaled to all heads; "
+                       f"est. {est_step:.1f} s per step"),
+            "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+
+
+# ----------------------------------------------------------------------------- #
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import gated_deltanet_03_amd as gdn
+    import gdn_inputs as gi
+
+    gdn.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    pre = gi.make("long_varlen")
+    dec = gi.make("spec_decode")
+    Hq, Hv, dk, dv, C = pre["Hq"], pre["Hv"], pre["dk"], pre["dv"], pre["chunk"]
+    es = 2
+    N = pre["num_seqs"]
+
+    # ---- resident device buffers (allocated before timing) --------------------
+    def devcopy(c):
+        return {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in c.items()}
+    pre_sets = [devcopy(pre) for _ in range(2)]
+    outs = [torch.empty_like(p["v"]) for p in pre_sets]
+    fins = [torch.empty((N, Hv, dk, dv), device=dev) for _ in range(2)]
+    snaps = [torch.empty_like(f) for f in fins]
+    sh = gdn.gdn_shape(N, pre["T"], Hq, Hv, dk, dv, pre["scale"], gdn.GDN_BF16)
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(sh, C, True), dtype=torch.uint8, device=dev)
+
+    d = devcopy(dec)
+    B, cap = dec["num_seqs"], dec["capacity"]
+    states = [d["s0"].clone() for _ in range(STATE_SETS)]
+    finals = [torch.empty_like(d["s0"]) for _ in range(STATE_SETS)]
+    R = Hv + Hq * dk + Hv * dv
+    su = torch.empty((B, cap, R), device=dev)
+    dec_o = torch.empty_like(d["v"])
+    counts = d["capture_count"]
+    dbytes, n_cap = decode_bytes(dec["lengths"], dec["capture_count"].tolist(), cap, Hq, Hv, dk, dv, es)
+    accept = torch.tensor(n_cap, dtype=torch.int32, device=dev)      # accept every captured token
+    rbytes = replay_bytes(n_cap, Hq, Hv, dk, dv)
+
+    def step(i):
+        p = pre_sets[i % 2]
+        gdn.gdn_prefill_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], scale=p["scale"],
+                                initial_state=p["s0"], cu_seqlens=p["cu_seqlens"], chunk_size=C,
+                                o=outs[i % 2], final_state=fins[i % 2], workspace=ws)
+        gdn.gdn_state_snapshot(fins[i % 2], snaps[i % 2])
+        j = i % STATE_SETS
+        gdn.gdn_recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+                               initial_state=states[j], cu_seqlens=d["cu_seqlens"], o=dec_o,
+                               final_state=finals[j], state_update_capacity=cap, capture_count=counts,
+                               state_update_active=1, state_update=su)
+        gdn.gdn_replay_state_updates(states[j], su, accept, Hq=Hq)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    gdn.gdn_profile_collect()          # drop anything recorded before
+    gdn.gdn_profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    gdn.gdn_profile_enable(False)
+    total_ms = ev0.elapsed_time(ev1)
+    prof = gdn.gdn_profile_collect()
+    ms_step = total_ms / args.steps
+
+    kernels = {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in prof.items()}
+    per_step_us = {k: 1000.0 * ms / args.steps for k, (n, ms) in prof.items()}
+
+    F = prefill_flops(pre["lengths"], C, Hq, Hv, dk, dv)
+    Fstate = state_kernel_flops(pre["lengths"], C, Hv, dk, dv)
+    Fprep = prep_kernel_flops(pre["lengths"], C, Hq, dk)
+    pbytes = prefill_bytes(pre["T"], N, Hq, Hv, dk, dv, es)
+    t_prefill_us = sum(per_step_us.get(k, 0.0) for k in ("chunk_plan_kernel", "chunk_prep_kernel",
+                                                          "chunk_state_kernel"))
+    t_dec_us = per_step_us.get("recurrent_step_kernel", float("nan"))
+    t_rep_us = per_step_us.get("replay_kernel", float("nan"))
+    t_snap_us = per_step_us.get("copy_kernel", float("nan"))
+
+    breakdown = {
+        "prefill": {"us": t_prefill_us, "tokens_per_s": pre["T"] / (t_prefill_us * 1e-6),
+                    "algorithmic_gflop": F / 1e9, "tflops": F / (t_prefill_us * 1e-6) / 1e12,
+                    "mfma_frac": F / (t_prefill_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+                    "algorithmic_mb": pbytes / 1e6,
+                    "hbm_frac": pbytes / (t_prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
+        "decode": {"us": t_dec_us, "tokens": dec["T"], "algorithmic_mb": dbytes / 1e6,
+                   "gbs": dbytes / (t_dec_us * 1e-6) / 1e9,
+                   "hbm_frac": dbytes / (t_dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
+        "replay": {"us": t_rep_us, "records": sum(n_cap), "algorithmic_mb": rbytes / 1e6,
+                   "gbs": rbytes / (t_rep_us * 1e-6) / 1e9,
+                   "hbm_frac": rbytes / (t_rep_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
+        "snapshot": {"us": t_snap_us, "gbs": 2 * N * Hv * dk * dv * 4 / (t_snap_us * 1e-6) / 1e9},
+    }
+
+    # dominant kernel: the one with the largest time per step
+    dom = max(per_step_us, key=per_step_us.get)
+    avg_s = kernels[dom]["avg_us"] * 1e-6
+    if dom == "chunk_state_kernel":
+        achieved, peak, unit, bound = Fstate / avg_s / 1e12, PEAK_MFMA_BF16_TFLOPS, "TFLOP/s", "mfma"
+    elif dom == "chunk_prep_kernel":
+        achieved, peak, unit, bound = Fprep / avg_s / 1e12, PEAK_MFMA_BF16_TFLOPS, "TFLOP/s", "mfma"
+    elif dom == "recurrent_step_kernel":
+        achieved, peak, unit, bound = dbytes / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    elif dom == "replay_kernel":
+        achieved, peak, unit, bound = rbytes / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = float("nan"), PEAK_HBM_GBS, "GB/s", "hbm"
+    roofline = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": committed_traffic(dom),
+                "avg_launch_us": kernels[dom]["avg_us"]}
+
+    tokens = pre["T"] + dec["T"]
+    out = {
+        "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("GDN hot path step: packed bf16 prefill 8192+5000+1031+63 tokens "
+                                "(Hq=16, Hv=32, dk=dv=128, chunk 64, initial+final states) + snapshot of "
+                                "the final states + ragged decode of 8 rows x <=7 tokens with capture "
+                                "(capacity 7) + replay of the captured prefix"),
+                   "prefill_tokens": pre["T"], "decode_tokens": dec["T"], "decode_lengths": dec["lengths"],
+                   "capture_counts": n_cap, "state_sets_rotated": STATE_SETS},
+        "roofline": roofline,
+        "breakdown": breakdown,
+        "kernels": kernels,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pre, dec, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,7 +29,7 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 _DTYPES = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 EXPORTED = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
             "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot",
-            "gdn_status_string", "gdn_last_error")
+            "gdn_status_string", "gdn_last_error", "gdn_profile_enable", "gdn_profile_collect")
 
 
 class gdn_shape(ctypes.Structure):
@@ -73,6 +73,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_status_string.argtypes = [i32]
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
+    lib.gdn_profile_enable.restype = i32
+    lib.gdn_profile_enable.argtypes = [i32]
+    lib.gdn_profile_collect.restype = i32
+    lib.gdn_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int32), i32]
     _lib = lib
     return lib
 
@@ -227,5 +232,21 @@ def gdn_state_snapshot(src, dst=None):
     return dst
 
 
-__all__ = ["load_library", "GdnError", "gdn_shape", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+def gdn_profile_enable(on: bool = True) -> None:
+    """Turn per-kernel HIP-event timing inside the library on or off."""
+    _check(load_library().gdn_profile_enable(int(bool(on))))
+
+
+def gdn_profile_collect() -> dict:
+    """{kernel name: (launches, total ms)} for the kernels timed since the last collect."""
+    lib = load_library()
+    n = 16
+    names = (ctypes.c_char_p * n)()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    k = lib.gdn_profile_collect(names, ms, cnt, n)
+    return {names[i].decode(): (int(cnt[i]), float(ms[i])) for i in range(min(k, n))}
+
+
+__all__ = ["gdn_profile_enable", "gdn_profile_collect", "load_library", "GdnError", "gdn_shape", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
            "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot", "EXPORTED", "LIB_PATH"]

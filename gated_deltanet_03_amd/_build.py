@@ -17,12 +17,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_profile.cpp", "gdn_recurrent.hip", "gdn_prefill.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are disabled for every HIP translation unit.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep MFMA accumulators in VGPRs (no AGPR round trips around VALU work)
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

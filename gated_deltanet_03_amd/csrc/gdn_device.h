@@ -75,6 +75,14 @@ __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d)
   }
 }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() carries a
+// workgroup-scope fence that also drains this wave's outstanding global loads
+// and stores (vmcnt); that would wait for register prefetches of the next chunk
+// and for output stores at every barrier.  Here only LDS operations (lgkmcnt)
+// are completed before the s_barrier; the clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Token range of sequence s: dense rows of T tokens when cu == nullptr, else
 // [cu[s], cu[s+1]) clamped to [0, total] so malformed offsets stay in bounds.
 __device__ __forceinline__ void seq_range(const int32_t* __restrict__ cu, int32_t T, int32_t total,

@@ -59,14 +59,22 @@ struct PrefillArgs {
 };
 
 // Per (chunk, value head) workspace block written by the chunk-prep kernel:
-//   A'  [64][64] element type (the UT inverse times diag(beta))
-//   MP  [64][64] element type (decay-masked Q K^T, lower triangle incl. diag)
+//   A'  6 x 512 elements: lower-triangular 16x32 blocks of the UT inverse times
+//       diag(beta), in MFMA fragment order
+//   MP  6 x 512 elements: the same blocks of the decay-masked Q K^T
 //   gam [64] fp32 (exp of the in-chunk cumulative log decay)
 //   tail[64] fp32 (exp(G_last - G_i), decay from token i to the chunk end)
 inline size_t chunk_block_bytes(DType dt) {
   size_t es = dt == DType::F32 ? 4 : 2;
-  return 64 * 64 * es * 2 + 64 * 4 * 2;
+  return 2 * 6 * 512 * es + 64 * 4 * 2;
 }
+
+// Opt-in per-kernel event timing (gdn_profile_enable / gdn_profile_collect).
+enum KernelId : int {
+  K_PLAN = 0, K_PREP, K_STATE, K_RECURRENT, K_ZERO_FILL, K_REPLAY, K_COPY, kNumKernels
+};
+void prof_begin(KernelId id, hipStream_t s);
+void prof_end(KernelId id, hipStream_t s);
 
 hipError_t launch_recurrent(DType dt, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_zero_fill(float* p, size_t n, hipStream_t s);

@@ -12,102 +12,139 @@
 //     slot 8g + j  <->  index  (j < 4 ? lo*16 + 4g + j : hi*16 + 4g + (j - 4)),
 // so that the B operand of a product can be taken straight from two fp32
 // accumulator tiles of an earlier product (lane l already holds rows 4g..4g+3 of
-// column l%16 in each), and the A operand is read as two 4-element runs from a
-// row-major matrix.  For fp32 the same 32-block is eight K=4 steps, step (t, q)
-// using accumulator element q of tile t and A[i][16t + 4g + q].
+// column l%16 in each), and an A operand is two 4-element runs of a row-major
+// matrix.  For fp32 the same 32-block is eight K=4 steps, step (t, q) using
+// accumulator element q of tile t and A[i][16t + 4g + q].
+//
+// A "fragment" is one lane's 8 operand values for one 16 x 32 block.  The
+// fragment-native storage of a block is 64 lanes x 8 consecutive elements, so a
+// whole block is read or written with one 16-byte (32-byte for fp32) access per
+// lane, conflict-free in LDS and fully coalesced in global memory.
 #pragma once
 
 #include "gdn_device.h"
 
 namespace gdn {
 
-template <typename T> struct Mfma;
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { bf16x8 v; };
+template <> struct Frag<_Float16> { f16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
 
-template <> struct Mfma<__bf16> {
-  static __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Mfma<_Float16> {
-  static __device__ __forceinline__ f32x4 mma(const f16x8& a, const f16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <typename T> struct Vec8;
-template <> struct Vec8<__bf16> { using type = bf16x8; using half = bf16x4; };
-template <> struct Vec8<_Float16> { using type = f16x8; using half = f16x4; };
-
-// 4 consecutive 16-bit elements (8 bytes, 8-byte aligned) from LDS or global.
-template <typename T>
-__device__ __forceinline__ typename Vec8<T>::half ld4(const T* p) {
-  return *reinterpret_cast<const typename Vec8<T>::half*>(p);
-}
+template <typename T> struct Half4;
+template <> struct Half4<__bf16> { using type = bf16x4; };
+template <> struct Half4<_Float16> { using type = f16x4; };
 
 template <typename T>
-__device__ __forceinline__ typename Vec8<T>::type cat(typename Vec8<T>::half lo, typename Vec8<T>::half hi) {
-  typename Vec8<T>::type r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
-
-template <typename T>
-__device__ __forceinline__ typename Vec8<T>::half cvt4(const f32x4& x) {
-  typename Vec8<T>::half r;
+__device__ __forceinline__ typename Half4<T>::type cvt4(const f32x4& x) {
+  typename Half4<T>::type r;
   r[0] = Elem<T>::from_f(x[0]); r[1] = Elem<T>::from_f(x[1]);
   r[2] = Elem<T>::from_f(x[2]); r[3] = Elem<T>::from_f(x[3]);
   return r;
 }
 
-// acc += A_blk * B_blk over one 32-wide contraction block.
-//   a_lo / a_hi: this lane's A row at contraction offsets (lo tile) 16*lo + 4g and
-//                (hi tile) 16*hi + 4g; 4 consecutive elements each.
-//   b_lo / b_hi: accumulator tiles holding B rows of the lo / hi tile.
-//   has_hi:      false when the hi tile does not exist (treated as zero).
+// Fragment from two accumulator tiles (the B operand of the next product).
 template <typename T>
-__device__ __forceinline__ void kblock_acc(f32x4& acc, const T* a_lo, const T* a_hi, const f32x4& b_lo,
-                                           const f32x4& b_hi, bool has_hi) {
+__device__ __forceinline__ Frag<T> make_frag(const f32x4& lo, const f32x4& hi) {
+  Frag<T> f;
   if constexpr (sizeof(T) == 4) {
-    const f32x4 al = *reinterpret_cast<const f32x4*>(a_lo);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(al[q], b_lo[q], acc, 0, 0, 0);
-    if (has_hi) {
-      const f32x4 ah = *reinterpret_cast<const f32x4*>(a_hi);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ah[q], b_hi[q], acc, 0, 0, 0);
-    }
+    f.lo = lo;
+    f.hi = hi;
   } else {
-    typename Vec8<T>::half zl = {}, al = ld4<T>(a_lo);
-    typename Vec8<T>::half ah = has_hi ? ld4<T>(a_hi) : zl;
-    typename Vec8<T>::half bh = has_hi ? cvt4<T>(b_hi) : zl;
-    acc = Mfma<T>::mma(cat<T>(al, ah), cat<T>(cvt4<T>(b_lo), bh), acc);
+    const auto a = cvt4<T>(lo), b = cvt4<T>(hi);
+    f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+    f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  }
+  return f;
+}
+
+// Fragment from two 4-element runs of a row-major matrix (A operand).
+template <typename T>
+__device__ __forceinline__ Frag<T> load_frag_rows(const T* lo, const T* hi) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 4) {
+    f.lo = *reinterpret_cast<const f32x4*>(lo);
+    f.hi = *reinterpret_cast<const f32x4*>(hi);
+  } else {
+    const auto a = *reinterpret_cast<const typename Half4<T>::type*>(lo);
+    const auto b = *reinterpret_cast<const typename Half4<T>::type*>(hi);
+    f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+    f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  }
+  return f;
+}
+
+// Fragment stored natively: 8 consecutive elements for this lane.
+template <typename T>
+__device__ __forceinline__ Frag<T> load_frag_native(const T* p) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 4) {
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  } else {
+    f.v = *reinterpret_cast<const decltype(f.v)*>(p);
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_frag_native(T* p, const Frag<T>& f) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(p) = f.lo;
+    *reinterpret_cast<f32x4*>(p + 4) = f.hi;
+  } else {
+    *reinterpret_cast<decltype(f.v)*>(const_cast<T*>(p)) = f.v;
   }
 }
 
-// acc += A_blk * B_blk where both operands are rows of row-major matrices
-// (B given as the rows of B^T, i.e. the product A * Bmat^T).
+// acc += A_blk * B_blk over one 32-wide contraction block.
 template <typename T>
-__device__ __forceinline__ void kblock_rows(f32x4& acc, const T* a_lo, const T* a_hi, const T* b_lo,
-                                            const T* b_hi, bool has_hi) {
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<T>& a, const Frag<T>& b) {
   if constexpr (sizeof(T) == 4) {
-    const f32x4 al = *reinterpret_cast<const f32x4*>(a_lo);
-    const f32x4 bl = *reinterpret_cast<const f32x4*>(b_lo);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(al[q], bl[q], acc, 0, 0, 0);
-    if (has_hi) {
-      const f32x4 ah = *reinterpret_cast<const f32x4*>(a_hi);
-      const f32x4 bh = *reinterpret_cast<const f32x4*>(b_hi);
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[q], b.lo[q], acc, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ah[q], bh[q], acc, 0, 0, 0);
-    }
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[q], b.hi[q], acc, 0, 0, 0);
+  } else if constexpr (__is_same(T, __bf16)) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
   } else {
-    typename Vec8<T>::half z = {};
-    typename Vec8<T>::half al = ld4<T>(a_lo), bl = ld4<T>(b_lo);
-    typename Vec8<T>::half ah = has_hi ? ld4<T>(a_hi) : z;
-    typename Vec8<T>::half bh = has_hi ? ld4<T>(b_hi) : z;
-    acc = Mfma<T>::mma(cat<T>(al, ah), cat<T>(bl, bh), acc);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
   }
+}
+
+// acc += A_blk * B_blk where only the lo tile of the block exists (the hi half
+// of both operands is zero): used for 16-wide contractions.
+template <typename T>
+__device__ __forceinline__ void mma_lo(f32x4& acc, const Frag<T>& a, const Frag<T>& b) {
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[q], b.lo[q], acc, 0, 0, 0);
+  } else {
+    mma<T>(acc, a, b);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> zero_frag() {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 4) {
+    f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+    f.hi = f.lo;
+  } else {
+    f.v = decltype(f.v){};
+  }
+  return f;
+}
+
+// The B fragment of the 16 x 16 identity restricted to the lo tile of a block:
+// slot 8g + j (j < 4) holds I[4g + j][n] = (4g + j == n); the hi half is zero.
+template <typename T>
+__device__ __forceinline__ Frag<T> identity_frag(int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  f32x4 lo;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lo[j] = (4 * g + j == n) ? 1.f : 0.f;
+  return make_frag<T>(lo, f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
 }  // namespace gdn

@@ -27,13 +27,22 @@
 // Kernel 3 never forms the W = A diag(beta gamma) K of the WY form: it applies
 // A' to the state-dependent right-hand side, so its chain per chunk is
 // K*S -> A'*X -> K^T*Delta, all on MFMA with fp32 accumulation.
+//
+// A' and MP are written in fragment-native order (gdn_mfma.h), lower-triangular
+// 16x32 blocks only: block (r, kb) with kb <= r/2, i.e. 6 blocks per matrix.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
 namespace gdn {
 
-constexpr int CMAX = 64;  // largest supported chunk (row tiles of 16)
+constexpr int NTRI = 6;   // lower-triangular 16x32 blocks of a 64x64 matrix
+constexpr int FRAG = 512; // elements per fragment-native block (64 lanes x 8)
+
+__device__ __forceinline__ int tri_idx(int r, int kb) { return r < 2 ? r : 2 * r - 2 + kb; }
+__device__ __forceinline__ void tri_rc(int f, int& r, int& kb) {
+  if (f < 2) { r = f; kb = 0; } else { r = (f + 2) >> 1; kb = f & 1; }
+}
 
 // ---------------------------------------------------------------------------
 // 1. plan
@@ -86,15 +95,15 @@ __device__ __forceinline__ int find_seq(const int32_t* off, int B, int gc) {
 
 template <typename T>
 struct Block {  // views of one (chunk, value head) workspace block
-  T* A;       // [64][64]
-  T* MP;      // [64][64]
-  float* gam; // [64]
-  float* tail;// [64]
+  T* A;        // NTRI fragment-native blocks of A'
+  T* MP;       // NTRI fragment-native blocks of MP
+  float* gam;  // [64]
+  float* tail; // [64]
   __device__ Block(void* base, size_t gc, int Hv, int h) {
-    char* b = static_cast<char*>(base) + (gc * Hv + h) * (64 * 64 * sizeof(T) * 2 + 512);
+    char* b = static_cast<char*>(base) + (gc * Hv + h) * (2 * NTRI * FRAG * sizeof(T) + 512);
     A = reinterpret_cast<T*>(b);
-    MP = A + 64 * 64;
-    gam = reinterpret_cast<float*>(MP + 64 * 64);
+    MP = A + NTRI * FRAG;
+    gam = reinterpret_cast<float*>(MP + NTRI * FRAG);
     tail = gam + 64;
   }
 };
@@ -102,31 +111,78 @@ struct Block {  // views of one (chunk, value head) workspace block
 // ---------------------------------------------------------------------------
 // 2. chunk prep: grid (max_chunks, Hq), 256 threads
 // ---------------------------------------------------------------------------
-template <typename T, int DK>
-struct PrepSmem {
-  static constexpr int KS = DK + 16 / (int)sizeof(T);  // padded row (16-byte aligned rows)
-  static constexpr int F = 65;                          // fp32 matrix row stride
-  // region 0: K and Q tiles during the Gram products; reused as Tm afterwards
-  static constexpr size_t kq_raw = 2 * 64 * KS * sizeof(T);
-  static constexpr size_t bytes_kq = kq_raw > 64 * F * 4 ? kq_raw : 64 * F * 4;
-  static constexpr size_t bytes_mats = 4 * 64 * F * 4;   // KK, P, Lm, Ai
-  static constexpr size_t total = bytes_kq + bytes_mats + 2 * 64 * 4;
-};
+constexpr int FS = 68;  // fp32 64x64 matrix row stride in LDS (16-byte aligned rows)
 
 template <typename T, int DK>
+struct PrepSmem {
+  static constexpr int KS = DK + 16 / (int)sizeof(T);  // padded K/Q rows (16-byte aligned)
+  static constexpr size_t mat = 64 * FS * 4;
+  static constexpr size_t kq = 2 * 64 * KS * sizeof(T);
+  // region A: Ks, Qs during the Gram products, then Lm and Ai
+  static constexpr size_t regA = kq > 2 * mat ? kq : 2 * mat;
+  // region B: KK and P; P is later reused as Tm
+  static constexpr size_t regB = 2 * mat;
+  static size_t total(int G) { return regA + regB + (size_t)G * 2 * 64 * 4; }
+};
+
+// One doubling level of the blocked inverse: for each pair of BS x BS diagonal
+// blocks (lo, hi) already inverted, A[hi, lo] = -A[hi,hi] L[hi,lo] A[lo,lo].
+template <int BS>
+__device__ __forceinline__ void inverse_level(const float* Lm, float* Ai, float* Tm, int npairs, int tid) {
+  constexpr int CPT = BS == 16 ? 2 : 4;    // output columns per thread
+  constexpr int CG = BS / CPT;
+  constexpr int PER = BS * CG;             // jobs per pair
+  for (int job = tid; job < npairs * PER; job += 256) {
+    const int pr = job / PER, rem = job % PER;
+    const int i = rem / CG, c = (rem % CG) * CPT;
+    const int r0 = (2 * pr + 1) * BS, c0 = 2 * pr * BS;
+    float acc[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) acc[u] = 0.f;
+#pragma unroll
+    for (int k = 0; k < BS; ++k) {
+      const float l = Lm[(r0 + i) * FS + c0 + k];
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) acc[u] = fmaf(l, Ai[(c0 + k) * FS + c0 + c + u], acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) Tm[(r0 + i) * FS + c0 + c + u] = acc[u];
+  }
+  lds_barrier();
+  for (int job = tid; job < npairs * PER; job += 256) {
+    const int pr = job / PER, rem = job % PER;
+    const int i = rem / CG, c = (rem % CG) * CPT;
+    const int r0 = (2 * pr + 1) * BS, c0 = 2 * pr * BS;
+    float acc[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) acc[u] = 0.f;
+#pragma unroll
+    for (int k = 0; k < BS; ++k) {
+      const float a = Ai[(r0 + i) * FS + r0 + k];
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) acc[u] = fmaf(a, Tm[(r0 + k) * FS + c0 + c + u], acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) Ai[(r0 + i) * FS + c0 + c + u] = -acc[u];
+  }
+  lds_barrier();
+}
+
+template <typename T, int DK, int C>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
   using SM = PrepSmem<T, DK>;
-  constexpr int KS = SM::KS, F = SM::F;
+  constexpr int KS = SM::KS;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* Ks = reinterpret_cast<T*>(smem_raw);
   T* Qs = Ks + 64 * KS;
-  float* KK = reinterpret_cast<float*>(smem_raw + SM::bytes_kq);
-  float* P = KK + 64 * F;
-  float* Lm = P + 64 * F;
-  float* Ai = Lm + 64 * F;
-  float* Tm = reinterpret_cast<float*>(smem_raw);  // aliases Ks/Qs after the Gram products
-  float* Gs = Ai + 64 * F;
-  float* Bs = Gs + 64;
+  float* Lm = reinterpret_cast<float*>(smem_raw);
+  float* Ai = Lm + 64 * FS;
+  float* KK = reinterpret_cast<float*>(smem_raw + SM::regA);
+  float* P = KK + 64 * FS;
+  float* Tm = P;
+  const int G = p.Hv / p.Hq;
+  float* Gs = P + 64 * FS;   // [G][64]
+  float* Bs = Gs + G * 64;   // [G][64]
 
   const int gc = blockIdx.x, hk = blockIdx.y;
   const int nchunks = p.chunk_offsets[p.B];
@@ -134,17 +190,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
   const int s = find_seq(p.chunk_offsets, p.B, gc);
   int st0, st1;
   seq_range(p.cu, p.T, p.total, s, st0, st1);
-  const int C = p.chunk;
+  constexpr int nrt = C / 16;
   const int t0 = st0 + (gc - p.chunk_offsets[s]) * C;
   const int len = min(C, st1 - t0);
-  const int nrt = C / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = p.Hv / p.Hq;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int i16 = lane & 15, g4 = lane >> 4;
 
   // ---- load K and Q rows (zero past the chunk end) -------------------------
   {
-    constexpr int PER = 16 / (int)sizeof(T);          // elements per 16-byte piece
-    constexpr int CPR = DK / PER;                     // pieces per row
+    constexpr int PER = 16 / (int)sizeof(T);
+    constexpr int CPR = DK / PER;
     const T* kp = static_cast<const T*>(p.k);
     const T* qp = static_cast<const T*>(p.q);
     for (int id = tid; id < 64 * CPR; id += 256) {
@@ -159,379 +215,499 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
       *reinterpret_cast<uint4*>(Qs + r * KS + c) = qv;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- Gram products on MFMA: KK = K K^T (tiles r >= c), P = Q K^T (r >= c) --
+  // ---- Gram products on MFMA: KK = K K^T and P = Q K^T, tiles (r, c) r >= c -
   {
-    const int i = lane & 15, g = lane >> 4;
     const int ntri = nrt * (nrt + 1) / 2;
     for (int job = wave; job < 2 * ntri; job += 4) {
       const bool isP = job >= ntri;
       int t = isP ? job - ntri : job, r = 0;
       while (t > r) { t -= r + 1; ++r; }
-      const int c = t;  // tile (r, c), r >= c
-      const T* A = isP ? Qs : Ks;
-      const T* arow = A + (16 * r + i) * KS;
-      const T* brow = Ks + (16 * c + i) * KS;
+      const int c = t;
+      const T* arow = (isP ? Qs : Ks) + (16 * r + i16) * KS + 4 * g4;
+      const T* brow = Ks + (16 * c + i16) * KS + 4 * g4;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < (DK + 31) / 32; ++kb) {
-        const bool hi = 32 * kb + 16 < DK;
-        kblock_rows<T>(acc, arow + 32 * kb + 4 * g, arow + 32 * kb + 16 + 4 * g, brow + 32 * kb + 4 * g,
-                       brow + 32 * kb + 16 + 4 * g, hi);
+      for (int kb = 0; kb < DK / 32; ++kb)
+        mma<T>(acc, load_frag_rows<T>(arow + 32 * kb, arow + 32 * kb + 16),
+               load_frag_rows<T>(brow + 32 * kb, brow + 32 * kb + 16));
+      if constexpr (DK == 16) {
+        Frag<T> a = load_frag_rows<T>(arow, arow), b = load_frag_rows<T>(brow, brow);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int j = 4; j < 8; ++j) { a.v[j] = 0; b.v[j] = 0; }
+        }
+        mma_lo<T>(acc, a, b);
       }
       float* D = isP ? P : KK;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) D[(16 * r + 4 * g + q) * F + 16 * c + i] = acc[q];
+      for (int q = 0; q < 4; ++q) D[(16 * r + 4 * g4 + q) * FS + 16 * c + i16] = acc[q];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  for (int vh = 0; vh < G; ++vh) {
-    const int h = hk * G + vh;
-    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
-    // ---- cumulative log decay over the chunk (wave 0) -----------------------
-    if (wave == 0) {
-      float gv = 0.f, bv = 0.f;
-      if (lane < len) {
-        gv = p.g[(size_t)(t0 + lane) * p.Hv + h];
-        bv = p.beta[(size_t)(t0 + lane) * p.Hv + h];
-      }
-      float x = gv;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      Gs[lane] = x;
-      Bs[lane] = bv;
-      const float glast = __shfl(x, C - 1);
-      blk.gam[lane] = expf(x);
-      blk.tail[lane] = expf(glast - x);
+  // ---- cumulative log decay per value head (one wave per head) -------------
+  for (int v = wave; v < G; v += 4) {
+    const int h = hk * G + v;
+    float gv = 0.f, bv = 0.f;
+    if (lane < len) {
+      gv = p.g[(size_t)(t0 + lane) * p.Hv + h];
+      bv = p.beta[(size_t)(t0 + lane) * p.Hv + h];
     }
-    __syncthreads();
-    // ---- L (strictly lower) in fp32, MP to the workspace ---------------------
+    float x = gv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    Gs[v * 64 + lane] = x;
+    Bs[v * 64 + lane] = bv;
+    const float glast = __shfl(x, C - 1);
+    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
+    blk.gam[lane] = expf(x);
+    blk.tail[lane] = expf(glast - x);
+  }
+  lds_barrier();
+
+  // ---- MP fragments for every value head of this key head ------------------
+  for (int job = tid; job < G * NTRI * 64; job += 256) {
+    const int v = job / (NTRI * 64), f = (job / 64) % NTRI, l = job & 63;
+    int r, kb;
+    tri_rc(f, r, kb);
+    const int row = 16 * r + (l & 15), gg = l >> 4;
+    const float* Gv = Gs + v * 64;
+    float val[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = 32 * kb + (j < 4 ? 4 * gg + j : 16 + 4 * gg + j - 4);
+      val[j] = (col <= row && row < C) ? expf(Gv[row] - Gv[col]) * P[row * FS + col] : 0.f;
+    }
+    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, hk * G + v);
+    store_frag_native<T>(blk.MP + (f * 64 + l) * 8,
+                         make_frag<T>(f32x4{val[0], val[1], val[2], val[3]}, f32x4{val[4], val[5], val[6], val[7]}));
+  }
+  lds_barrier();   // P is dead from here on (its space becomes Tm)
+
+  for (int v = 0; v < G; ++v) {
+    const int h = hk * G + v;
+    const float* Gv = Gs + v * 64;
+    const float* Bv = Bs + v * 64;
+    // ---- L (strictly lower, beta-scaled, decay-weighted) and A := 0 ---------
     for (int idx = tid; idx < 64 * 64; idx += 256) {
       const int i = idx >> 6, j = idx & 63;
       float l = 0.f;
-      if (j < i && i < C) l = Bs[i] * expf(Gs[i] - Gs[j]) * KK[i * F + j];
-      Lm[i * F + j] = l;
-      Ai[i * F + j] = 0.f;
+      if (j < i && i < C) l = Bv[i] * expf(Gv[i] - Gv[j]) * KK[i * FS + j];
+      Lm[i * FS + j] = l;
+      Ai[i * FS + j] = 0.f;
     }
-    {
-      // MP rows: thread handles 16 consecutive columns of one row
-      const int i = tid >> 2, j0 = (tid & 3) * 16;
-      float vals[16];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int j = j0 + jj;
-        vals[jj] = (j <= i && i < C) ? expf(Gs[i] - Gs[j]) * P[i * F + j] : 0.f;
-      }
-      T* dst = blk.MP + i * 64 + j0;
-#pragma unroll
-      for (int jj = 0; jj < 16; jj += 4) store4<T>(dst + jj, vals[jj], vals[jj + 1], vals[jj + 2], vals[jj + 3]);
-    }
-    __syncthreads();
-    // ---- UT inverse A = (I + L)^-1, blocked: 16x16 diagonal blocks by forward
-    //      substitution, then doubling: A_hi,lo = -A_hi * L_hi,lo * A_lo -------
+    lds_barrier();
+    // ---- 16x16 diagonal blocks by forward substitution (lane = column) -----
     if (wave < nrt && lane < 16) {
       const int b0 = 16 * wave, c = lane;
       float x[16];
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
+        float Lr[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; jj += 4) {
+          const float4 w = *reinterpret_cast<const float4*>(&Lm[(b0 + ii) * FS + b0 + jj]);
+          Lr[jj] = w.x; Lr[jj + 1] = w.y; Lr[jj + 2] = w.z; Lr[jj + 3] = w.w;
+        }
         float acc = (ii == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int jj = 0; jj < ii; ++jj) acc = fmaf(-Lm[(b0 + ii) * F + b0 + jj], x[jj], acc);
+        for (int jj = 0; jj < ii; ++jj) acc = fmaf(-Lr[jj], x[jj], acc);
         x[ii] = acc;
       }
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) Ai[(b0 + ii) * F + b0 + c] = x[ii];
+      for (int ii = 0; ii < 16; ++ii) Ai[(b0 + ii) * FS + b0 + c] = x[ii];
     }
-    __syncthreads();
-    for (int bs = 16; 2 * bs <= C; bs *= 2) {
-      const int npairs = C / (2 * bs);
-      const int nout = npairs * bs * bs;
-      // Tm = L_hi,lo * A_lo
-      for (int idx = tid; idx < nout; idx += 256) {
-        const int pr = idx / (bs * bs), rem = idx % (bs * bs);
-        const int ii = rem / bs, cc = rem % bs;
-        const int r0 = (2 * pr + 1) * bs, c0 = 2 * pr * bs;
-        float acc = 0.f;
-        for (int kk = cc; kk < bs; ++kk) acc = fmaf(Lm[(r0 + ii) * F + c0 + kk], Ai[(c0 + kk) * F + c0 + cc], acc);
-        Tm[(r0 + ii) * F + c0 + cc] = acc;
-      }
-      __syncthreads();
-      // A_hi,lo = -A_hi * Tm
-      for (int idx = tid; idx < nout; idx += 256) {
-        const int pr = idx / (bs * bs), rem = idx % (bs * bs);
-        const int ii = rem / bs, cc = rem % bs;
-        const int r0 = (2 * pr + 1) * bs, c0 = 2 * pr * bs;
-        float acc = 0.f;
-        for (int kk = 0; kk <= ii; ++kk) acc = fmaf(Ai[(r0 + ii) * F + r0 + kk], Tm[(r0 + kk) * F + c0 + cc], acc);
-        Ai[(r0 + ii) * F + c0 + cc] = -acc;
-      }
-      __syncthreads();
-    }
-    // ---- A' = A diag(beta) to the workspace -----------------------------------
+    lds_barrier();
+    // ---- doubling: 16 -> 32 -> 64 ------------------------------------------
+    if (C >= 32) inverse_level<16>(Lm, Ai, Tm, C / 32, tid);
+    if (C >= 64) inverse_level<32>(Lm, Ai, Tm, 1, tid);
+    // ---- A' = A diag(beta) as fragment-native lower-triangular blocks -------
     {
-      const int i = tid >> 2, j0 = (tid & 3) * 16;
-      T* dst = blk.A + i * 64 + j0;
+      Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
+      for (int job = tid; job < NTRI * 64; job += 256) {
+        const int f = job / 64, l = job & 63;
+        int r, kb;
+        tri_rc(f, r, kb);
+        const int row = 16 * r + (l & 15), gg = l >> 4;
+        float val[8];
 #pragma unroll
-      for (int jj = 0; jj < 16; jj += 4) {
-        float v4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = j0 + jj + u;
-          v4[u] = (i < C && j < C) ? Ai[i * F + j] * Bs[j] : 0.f;
+        for (int j = 0; j < 8; ++j) {
+          const int col = 32 * kb + (j < 4 ? 4 * gg + j : 16 + 4 * gg + j - 4);
+          val[j] = (row < C && col < C) ? Ai[row * FS + col] * Bv[col] : 0.f;
         }
-        store4<T>(dst + jj, v4[0], v4[1], v4[2], v4[3]);
+        store_frag_native<T>(blk.A + (f * 64 + l) * 8,
+                             make_frag<T>(f32x4{val[0], val[1], val[2], val[3]},
+                                          f32x4{val[4], val[5], val[6], val[7]}));
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. state pass: grid (slices of 64 columns, Hv, B), 64 * NW threads
+// 3. state pass: grid (slices of 64 columns, Hv, B), 256 threads (4 waves x 16
+//    columns).  Chunk inputs are staged with direct global->LDS loads
+//    (global_load_lds_dwordx4: each wave instruction writes 64 lanes x 16 bytes
+//    contiguously at a wave-uniform LDS address), double-buffered so that chunk
+//    c+1 streams in while chunk c computes.  Row-major tiles are XOR-swizzled
+//    per 16-byte piece (piece p of row r lives at piece p ^ (r mod pieces-per-row))
+//    so that MFMA fragment reads of 16 consecutive rows hit distinct banks.
+//    Rows past a sequence's end are loaded from its last row instead of being
+//    zeroed: A' and MP carry exact zeros in those rows and columns, so the
+//    finite stand-in values never reach an output.
 // ---------------------------------------------------------------------------
+// One wave instruction: every lane copies 16 bytes from its src to
+// lds + 16 * lane (lds must be wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 template <typename T, int DK>
 struct StateSmem {
-  static constexpr int PADE = 16 / (int)sizeof(T);
-  static constexpr int KS = DK + PADE;      // K, Q row-major [64][KS]
-  static constexpr int TS = 64 + PADE;      // K^T [DK][TS], A', MP [64][TS], V^T [64][TS]
-  static constexpr size_t total =
-      (size_t)(2 * 64 * KS + DK * TS + 3 * 64 * TS) * sizeof(T) + 2 * 64 * 4;
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int PER = 16 / ES;               // elements per 16-byte piece
+  static constexpr int PPR = DK / PER;              // pieces per K/Q row
+  static constexpr int ROWB = DK * ES;              // bytes per K/Q row
+  static constexpr int NST = DK / 16;               // state row tiles
+  static constexpr int NKT = 2 * NST;               // K^T fragments (dk tile, token block)
+  static constexpr int KB = 64 * ROWB;              // K (or Q) tile bytes
+  static constexpr int VB = 64 * 64 * ES;           // V tile bytes (up to 64 columns)
+  static constexpr int AB = 2 * NTRI * FRAG * ES;   // A' and MP fragments
+  static constexpr int STAGE = 2 * KB + VB + AB + 512;
+  static constexpr int KTB = NKT * FRAG * ES;
+  static constexpr int NBUF = 2 * STAGE + KTB <= 160 * 1024 ? 2 : 1;
+  static constexpr size_t total = (size_t)NBUF * STAGE + KTB;
+  // byte offsets inside one stage buffer
+  static constexpr int OK_ = 0, OQ = KB, OV = 2 * KB, OA = 2 * KB + VB, OG = 2 * KB + VB + AB;
 };
 
-template <typename T, int DK>
+template <typename T, int DK, int C>
 __global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs p) {
   using SM = StateSmem<T, DK>;
-  constexpr int KS = SM::KS, TS = SM::TS, NST = DK / 16;
-  constexpr int PER = 16 / (int)sizeof(T);
+  constexpr int nrt = C / 16;
+  constexpr int NST = SM::NST, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
+  constexpr int NSB = (NST + 1) / 2;      // 32-wide blocks of the dk contraction
+  constexpr int RPI_K = 64 / PPR;         // K rows per DMA instruction
+  constexpr int NA = SM::AB / 1024;       // DMA instructions for A' and MP
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* Ks = reinterpret_cast<T*>(smem_raw);
-  T* Qs = Ks + 64 * KS;
-  T* Kt = Qs + 64 * KS;
-  T* As = Kt + DK * TS;
-  T* MPs = As + 64 * TS;
-  T* Vt = MPs + 64 * TS;
-  float* gam_s = reinterpret_cast<float*>(Vt + 64 * TS);
-  float* tail_s = gam_s + 64;
+  unsigned char* KTbytes = smem_raw + SM::NBUF * SM::STAGE;
+  T* KT = reinterpret_cast<T*>(KTbytes);
 
   const int slice = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthreads = blockDim.x;
-  const int ncols = min(64, p.dv - 64 * slice);   // columns of this slice (16 * waves)
-  const int col0 = 64 * slice + 16 * wave;        // this wave's 16 columns
-  const int i16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int ncols = min(64, p.dv - 64 * slice);
+  const int col0 = 64 * slice + 16 * wave;
+  const bool active = 16 * wave < ncols;   // slices narrower than 64 columns idle some waves
+  const int i16 = lane & 15, g4 = lane >> 4;
   const int hk = h / (p.Hv / p.Hq);
-  const int C = p.chunk, nrt = C / 16;
   const int dv = p.dv;
+  const int pprv = ncols / PER;           // pieces per V row (power of two)
+  const int rowbv = ncols * ES;           // bytes per V row
+  const int rpiv = 64 / pprv;             // V rows per DMA instruction
 
   int st0, st1;
   seq_range(p.cu, p.T, p.total, s, st0, st1);
   const int cbeg = p.chunk_offsets[s];
   const int nch = p.chunk_offsets[s + 1] - cbeg;
 
-  // State tiles: tile r holds rows 16r + 4g + q, column col0 + i16.
-  f32x4 S[NST];
-  if (p.s0 != nullptr) {
-    const float* s0 = p.s0 + (int64_t)s * p.s0_stride + ((size_t)h * DK) * dv + col0 + i16;
-#pragma unroll
-    for (int r = 0; r < NST; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) S[r][q] = s0[(size_t)(16 * r + 4 * g + q) * dv];
-  } else {
-#pragma unroll
-    for (int r = 0; r < NST; ++r) S[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
   const T* kp = static_cast<const T*>(p.k);
   const T* qp = static_cast<const T*>(p.q);
   const T* vp = static_cast<const T*>(p.v);
   T* op = static_cast<T*>(p.o);
 
-  for (int c = 0; c < nch; ++c) {
+  // ---- this wave's DMA slots (compile-time counts, loop-invariant offsets) ----
+  // K and Q: PPR instructions each (RPI_K rows per 1 KB), V: pprv instructions,
+  // A'/MP: NA instructions, gamma/tail: half an instruction (wave 3).
+  constexpr int KPW = (PPR + 3) / 4, VPW = (64 / PER + 3) / 4, APW = (NA + 3) / 4;
+  int krow[KPW], koff[KPW], vrow[VPW], voff[VPW];
+#pragma unroll
+  for (int m = 0; m < KPW; ++m) {
+    const int j = wave + 4 * m;
+    const int r = RPI_K * j + lane / PPR;
+    const int pp = (lane % PPR) ^ (r % PPR);           // logical piece stored at this slot
+    krow[m] = r;
+    koff[m] = (r * p.Hq + hk) * DK + pp * PER;
+  }
+#pragma unroll
+  for (int m = 0; m < VPW; ++m) {
+    const int j = wave + 4 * m;
+    const int r = rpiv * j + lane / pprv;
+    const int pp = (lane % pprv) ^ (r % pprv);
+    vrow[m] = r;
+    voff[m] = (r * p.Hv + h) * dv + 64 * slice + pp * PER;
+  }
+  const int kq_row_stride = p.Hq * DK, v_row_stride = p.Hv * dv;
+  auto issue = [&](int c, int buf) {
     const int t0 = st0 + c * C;
-    const int len = min(C, st1 - t0);
+    const int last = min(C, st1 - t0) - 1;
+    const bool full = last == C - 1;                   // no row of this chunk needs clamping
+    unsigned char* sb = smem_raw + buf * SM::STAGE;
+    const T* kc = kp + (size_t)t0 * kq_row_stride;
+    const T* qc = qp + (size_t)t0 * kq_row_stride;
+    const T* vc = vp + (size_t)t0 * v_row_stride;
     Block<T> blk(p.chunk_data, (size_t)(cbeg + c), p.Hv, h);
-    __syncthreads();  // previous chunk's readers are done with the LDS tiles
-    // ---- stage K (row-major and transposed), Q, A', MP, V^T, gamma, tail ----
-    {
-      constexpr int CPR = DK / PER;
-      for (int id = tid; id < 64 * CPR; id += nthreads) {
-        const int r = id / CPR, cc = (id % CPR) * PER;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-        if (r < len) {
-          const size_t off = ((size_t)(t0 + r) * p.Hq + hk) * DK + cc;
-          kv = *reinterpret_cast<const uint4*>(kp + off);
-          qv = *reinterpret_cast<const uint4*>(qp + off);
-        }
-        *reinterpret_cast<uint4*>(Ks + r * KS + cc) = kv;
-        *reinterpret_cast<uint4*>(Qs + r * KS + cc) = qv;
-        const T* ke = reinterpret_cast<const T*>(&kv);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) Kt[(cc + e) * TS + r] = ke[e];
-      }
-      constexpr int CPM = 64 / PER;  // pieces per 64-wide row
-      for (int id = tid; id < 64 * CPM; id += nthreads) {
-        const int r = id / CPM, cc = (id % CPM) * PER;
-        *reinterpret_cast<uint4*>(As + r * TS + cc) = *reinterpret_cast<const uint4*>(blk.A + r * 64 + cc);
-        *reinterpret_cast<uint4*>(MPs + r * TS + cc) = *reinterpret_cast<const uint4*>(blk.MP + r * 64 + cc);
-      }
-      const int vpr = ncols / PER;   // pieces per token row of this slice
-      for (int id = tid; id < 64 * vpr; id += nthreads) {
-        const int r = id / vpr, cc = (id % vpr) * PER;
-        uint4 vv = make_uint4(0, 0, 0, 0);
-        if (r < len) vv = *reinterpret_cast<const uint4*>(vp + ((size_t)(t0 + r) * p.Hv + h) * dv + 64 * slice + cc);
-        const T* ve = reinterpret_cast<const T*>(&vv);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) Vt[(cc + e) * TS + r] = ve[e];
-      }
-      if (tid < 64) {
-        gam_s[tid] = blk.gam[tid];
-        tail_s[tid] = blk.tail[tid];
+    for (int m = 0; m < KPW; ++m) {
+      const int j = wave + 4 * m;
+      if (j < PPR) {
+        const int off = full ? koff[m] : koff[m] + (min(krow[m], last) - krow[m]) * kq_row_stride;
+        dma16(kc + off, sb + SM::OK_ + j * 1024);
+        dma16(qc + off, sb + SM::OQ + j * 1024);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < VPW; ++m) {
+      const int j = wave + 4 * m;
+      if (j < pprv) {
+        const int off = full ? voff[m] : voff[m] + (min(vrow[m], last) - vrow[m]) * v_row_stride;
+        dma16(vc + off, sb + SM::OV + j * 1024);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < APW; ++m) {
+      const int j = wave + 4 * m;
+      if (j < NA) dma16(blk.A + (j * 64 + lane) * PER, sb + SM::OA + j * 1024);
+    }
+    if (wave == 3 && lane < 32) dma16(blk.gam + 4 * lane, sb + SM::OG);
+  };
 
-    // ---- KS = K S and QS = Q S (contraction over dk) -------------------------
+  // State tiles: tile r holds rows 16r + 4g + q of column col0 + i16.
+  f32x4 S[NST];
+  if (p.s0 != nullptr && active) {
+    const float* s0 = p.s0 + (int64_t)s * p.s0_stride + ((size_t)h * DK) * dv + col0 + i16;
+#pragma unroll
+    for (int r = 0; r < NST; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) S[r][q] = s0[(size_t)(16 * r + 4 * g4 + q) * dv];
+  } else {
+#pragma unroll
+    for (int r = 0; r < NST; ++r) S[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const Frag<T> ident = identity_frag<T>(lane);
+  // this lane's o offset inside a chunk: token 4g + q (+16r), column col0 + i16
+  const size_t ostride = (size_t)p.Hv * dv;
+  const size_t olane = (size_t)(4 * g4) * ostride + (size_t)h * dv + col0 + i16;
+  if (nch > 0) issue(0, 0);
+
+  for (int c = 0; c < nch; ++c) {
+    const int buf = SM::NBUF == 2 ? (c & 1) : 0;
+    const int t0 = st0 + c * C;
+    const int len = min(C, st1 - t0);
+    // chunk c has landed in LDS for every wave; every wave is done with chunk c-1
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
+    const unsigned char* sb = smem_raw + buf * SM::STAGE;
+    const T* Ks = reinterpret_cast<const T*>(sb + SM::OK_);
+    const T* Qs = reinterpret_cast<const T*>(sb + SM::OQ);
+    const T* Vs = reinterpret_cast<const T*>(sb + SM::OV);
+    const T* AMP = reinterpret_cast<const T*>(sb + SM::OA);
+    const float* GT = reinterpret_cast<const float*>(sb + SM::OG);
+    // element e of K/Q row r (e a multiple of 4): swizzled piece address
+    auto rowp = [&](const T* tile, int r, int e) {
+      const int b = e * ES;
+      return reinterpret_cast<const T*>(reinterpret_cast<const unsigned char*>(tile) + r * SM::ROWB +
+                                        ((((b >> 4) ^ (r % PPR))) << 4) + (b & 15));
+    };
+
+    // ---- K^T fragments by identity products, shared through LDS -------------
+    //      fragment (dk tile rt, token block kb): lo = K[32kb + 4g + j][16rt + n],
+    //      hi = K[32kb + 16 + 4g + j][16rt + n], i.e. tiles D(t, rt) of K * I.
+#pragma unroll
+    for (int f0 = 0; f0 < SM::NKT; f0 += 4) {
+      const int f = f0 + wave;
+      if (f < SM::NKT) {
+        const int rt = f >> 1, kb = f & 1;
+        f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+        if (2 * kb < nrt) {
+          const T* a = rowp(Ks, 32 * kb + i16, 16 * rt + 4 * g4);
+          Frag<T> fa = load_frag_rows<T>(a, a);
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int j = 4; j < 8; ++j) fa.v[j] = 0;
+          }
+          mma_lo<T>(lo, fa, ident);
+        }
+        if (2 * kb + 1 < nrt) {
+          const T* a = rowp(Ks, 32 * kb + 16 + i16, 16 * rt + 4 * g4);
+          Frag<T> fa = load_frag_rows<T>(a, a);
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int j = 4; j < 8; ++j) fa.v[j] = 0;
+          }
+          mma_lo<T>(hi, fa, ident);
+        }
+        store_frag_native<T>(KT + (f * 64 + lane) * 8, make_frag<T>(lo, hi));
+      }
+    }
+
+    // ---- B fragments of the state -------------------------------------------
+    Frag<T> Sb[NSB];
+#pragma unroll
+    for (int kb = 0; kb < NSB; ++kb)
+      Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
+    // ---- KS = K S and QS = Q S: all row tiles advance together per k-block ---
     f32x4 KSa[4], QSa[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       KSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
       QSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (r < nrt) {
-        const T* krow = Ks + (16 * r + i16) * KS + 4 * g;
-        const T* qrow = Qs + (16 * r + i16) * KS + 4 * g;
+    }
 #pragma unroll
-        for (int kb = 0; kb < (NST + 1) / 2; ++kb) {
-          const bool hi = 2 * kb + 1 < NST;
-          const f32x4 bh = hi ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f};
-          kblock_acc<T>(KSa[r], krow + 32 * kb, krow + 32 * kb + 16, S[2 * kb], bh, hi);
-          kblock_acc<T>(QSa[r], qrow + 32 * kb, qrow + 32 * kb + 16, S[2 * kb], bh, hi);
+    for (int kb = 0; kb < NSB; ++kb) {
+      const int hoff = 2 * kb + 1 < NST ? 32 * kb + 16 : 32 * kb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < nrt) {
+          const int row = 16 * r + i16;
+          mma<T>(KSa[r], load_frag_rows<T>(rowp(Ks, row, 32 * kb + 4 * g4), rowp(Ks, row, hoff + 4 * g4)), Sb[kb]);
+          mma<T>(QSa[r], load_frag_rows<T>(rowp(Qs, row, 32 * kb + 4 * g4), rowp(Qs, row, hoff + 4 * g4)), Sb[kb]);
         }
       }
     }
-    // ---- X = V - gamma * KS (accumulator layout: token 16r+4g+q, column i16) --
+    // ---- X = V - gamma * KS ---------------------------------------------------
     f32x4 X[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       X[r] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (r < nrt) {
-        const T* vrow = Vt + (16 * wave + i16) * TS + 16 * r + 4 * g;
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+        const int cb = (16 * wave + i16) * ES;          // byte of this column inside a V row
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int tok = 16 * r + 4 * g + q;
-          X[r][q] = Elem<T>::to_f(vrow[q]) - gam_s[tok] * KSa[r][q];
+          const int tok = 16 * r + 4 * g4 + q;
+          const T* vv = reinterpret_cast<const T*>(reinterpret_cast<const unsigned char*>(Vs) + tok * rowbv +
+                                                   ((((cb >> 4) ^ (tok & (pprv - 1)))) << 4) + (cb & 15));
+          X[r][q] = Elem<T>::to_f(*vv) - gm[q] * KSa[r][q];
         }
       }
     }
-    // ---- Delta = A' X (A' lower triangular: only blocks kb <= r/2) ----------
+    const Frag<T> Xb0 = make_frag<T>(X[0], X[1]), Xb1 = make_frag<T>(X[2], X[3]);
+    // ---- Delta = A' X ---------------------------------------------------------
     f32x4 D[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       D[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (r < nrt) {
-        const T* arow = As + (16 * r + i16) * TS + 4 * g;
-#pragma unroll
-        for (int kb = 0; kb <= r / 2; ++kb) {
-          const bool hi = 2 * kb + 1 < nrt;
-          kblock_acc<T>(D[r], arow + 32 * kb, arow + 32 * kb + 16, X[2 * kb], X[(2 * kb + 1) & 3], hi);
-        }
-      }
+      if (r < nrt) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8), Xb0);
     }
-    // ---- O = scale (gamma QS + MP Delta) -> o --------------------------------
+#pragma unroll
+    for (int r = 2; r < 4; ++r)
+      if (r < nrt) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8), Xb1);
+    const Frag<T> Db0 = make_frag<T>(D[0], D[1]), Db1 = make_frag<T>(D[2], D[3]);
+    // ---- O = scale (gamma QS + MP Delta) -> o ----------------------------------
+    f32x4 O[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (r < nrt) {
-        f32x4 O;
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) O[q] = gam_s[16 * r + 4 * g + q] * QSa[r][q];
-        const T* mrow = MPs + (16 * r + i16) * TS + 4 * g;
-#pragma unroll
-        for (int kb = 0; kb <= r / 2; ++kb) {
-          const bool hi = 2 * kb + 1 < nrt;
-          kblock_acc<T>(O, mrow + 32 * kb, mrow + 32 * kb + 16, D[2 * kb], D[(2 * kb + 1) & 3], hi);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int tok = 16 * r + 4 * g + q;
-          if (tok < len) op[((size_t)(t0 + tok) * p.Hv + h) * dv + col0 + i16] = Elem<T>::from_f(p.scale * O[q]);
-        }
-      }
+      for (int q = 0; q < 4; ++q) O[r][q] = gm[q] * QSa[r][q];
+      if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 0)) * 64 + lane) * 8), Db0);
     }
-    // ---- S = gamma_last S + K^T (tail * Delta) --------------------------------
-    const float gl = gam_s[C - 1];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 2; r < 4; ++r)
+      if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 1)) * 64 + lane) * 8), Db1);
+    if (active) {
+      T* oc = op + (size_t)t0 * ostride + olane;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) D[r][q] *= tail_s[16 * r + 4 * g + q];
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int r = 0; r < NST; ++r) {
+        for (int q = 0; q < 4; ++q)
+          if (16 * r + 4 * g4 + q < len) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
+    }
+    // ---- tail-weighted Delta ---------------------------------------------------
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 tl = *reinterpret_cast<const f32x4*>(GT + 64 + 16 * r + 4 * g4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) D[r][q] *= tl[q];
+    }
+    const Frag<T> Tb0 = make_frag<T>(D[0], D[1]), Tb1 = make_frag<T>(D[2], D[3]);
+    const float gl = GT[C - 1];
+    lds_barrier();   // K^T fragments of every wave are in LDS; stage reads are done
+    if (SM::NBUF == 1 && c + 1 < nch) issue(c + 1, 0);
+    // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
+#pragma unroll
+    for (int r = 0; r < NST; ++r)
 #pragma unroll
       for (int q = 0; q < 4; ++q) S[r][q] *= gl;
-      const T* ktrow = Kt + (16 * r + i16) * TS + 4 * g;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (2 * kb < nrt) {
-          const bool hi = 2 * kb + 1 < nrt;
-          kblock_acc<T>(S[r], ktrow + 32 * kb, ktrow + 32 * kb + 16, D[2 * kb], D[2 * kb + 1], hi);
-        }
+    for (int kb = 0; kb < 2; ++kb) {
+      if (2 * kb < nrt) {
+#pragma unroll
+        for (int r = 0; r < NST; ++r)
+          mma<T>(S[r], load_frag_native<T>(KT + ((2 * r + kb) * 64 + lane) * 8), kb == 0 ? Tb0 : Tb1);
       }
     }
   }
 
-  if (p.s_out != nullptr) {
+  if (p.s_out != nullptr && active) {
     float* so = p.s_out + ((size_t)s * p.Hv + h) * DK * dv + col0 + i16;
 #pragma unroll
     for (int r = 0; r < NST; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) so[(size_t)(16 * r + 4 * g + q) * dv] = S[r][q];
+      for (int q = 0; q < 4; ++q) so[(size_t)(16 * r + 4 * g4 + q) * dv] = S[r][q];
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
-template <typename T, int DK>
+template <typename T, int DK, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  prof_begin(K_PLAN, st);
   hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a);
+  prof_end(K_PLAN, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 0) {
-    const size_t sm1 = PrepSmem<T, DK>::total;
-    static bool attr1 = false;
-    if (!attr1) {
-      e = hipFuncSetAttribute((const void*)chunk_prep_kernel<T, DK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)sm1);
-      if (e != hipSuccess) return e;
-      attr1 = true;
-    }
-    hipLaunchKernelGGL((chunk_prep_kernel<T, DK>), dim3(a.max_chunks, a.Hq), dim3(256), sm1, st, a);
+    const size_t sm1 = PrepSmem<T, DK>::total(a.Hv / a.Hq);
+    if (sm1 > 160 * 1024) return hipErrorInvalidValue;
+    e = hipFuncSetAttribute((const void*)chunk_prep_kernel<T, DK, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sm1);
+    if (e != hipSuccess) return e;
+    prof_begin(K_PREP, st);
+    hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C>), dim3(a.max_chunks, a.Hq), dim3(256), sm1, st, a);
+    prof_end(K_PREP, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int nslices = (a.dv + 63) / 64;
-  const int nw = a.dv >= 64 ? 4 : a.dv / 16;
   const size_t sm2 = StateSmem<T, DK>::total;
   static bool attr2 = false;
   if (!attr2) {
-    e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sm2);
     if (e != hipSuccess) return e;
     attr2 = true;
   }
-  hipLaunchKernelGGL((chunk_state_kernel<T, DK>), dim3(nslices, a.Hv, a.B), dim3(64 * nw), sm2, st, a);
+  prof_begin(K_STATE, st);
+  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C>), dim3(nslices, a.Hv, a.B), dim3(256), sm2, st, a);
+  prof_end(K_STATE, st);
   return hipGetLastError();
+}
+
+template <typename T, int DK>
+static hipError_t launch_prefill_c(const PrefillArgs& a, hipStream_t st) {
+  switch (a.chunk) {
+    case 16: return launch_prefill_t<T, DK, 16>(a, st);
+    case 32: return launch_prefill_t<T, DK, 32>(a, st);
+    case 64: return launch_prefill_t<T, DK, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
 static hipError_t launch_prefill_dt(const PrefillArgs& a, hipStream_t st) {
   switch (a.dk) {
-    case 16: return launch_prefill_t<T, 16>(a, st);
-    case 32: return launch_prefill_t<T, 32>(a, st);
-    case 64: return launch_prefill_t<T, 64>(a, st);
-    case 128: return launch_prefill_t<T, 128>(a, st);
+    case 16: return launch_prefill_c<T, 16>(a, st);
+    case 32: return launch_prefill_c<T, 32>(a, st);
+    case 64: return launch_prefill_c<T, 64>(a, st);
+    case 128: return launch_prefill_c<T, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }

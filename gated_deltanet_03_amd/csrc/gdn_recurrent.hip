@@ -225,6 +225,7 @@ __global__ __launch_bounds__(256) void copy_kernel(const float* __restrict__ src
 template <typename T, int DK>
 static hipError_t launch_rec_dk(const DecodeArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
+  prof_begin(K_RECURRENT, s);
   if (a.dv >= 32) {
     dim3 grid(a.dv / 32, a.Hv, a.B);
     hipLaunchKernelGGL((recurrent_step_kernel<T, DK, 32>), grid, dim3(64), 0, s, a);
@@ -232,6 +233,7 @@ static hipError_t launch_rec_dk(const DecodeArgs& a, hipStream_t s) {
     dim3 grid(a.dv / 16, a.Hv, a.B);
     hipLaunchKernelGGL((recurrent_step_kernel<T, DK, 16>), grid, dim3(64), 0, s, a);
   }
+  prof_end(K_RECURRENT, s);
   return hipGetLastError();
 }
 
@@ -258,11 +260,13 @@ hipError_t launch_recurrent(DType dt, const DecodeArgs& a, hipStream_t s) {
 template <int DK>
 static hipError_t launch_replay_dk(const ReplayArgs& a, hipStream_t s) {
   if (a.B == 0 || a.cap == 0) return hipSuccess;
+  prof_begin(K_REPLAY, s);
   if (a.dv >= 32) {
     hipLaunchKernelGGL((replay_kernel<DK, 32>), dim3(a.dv / 32, a.Hv, a.B), dim3(64), 0, s, a);
   } else {
     hipLaunchKernelGGL((replay_kernel<DK, 16>), dim3(a.dv / 16, a.Hv, a.B), dim3(64), 0, s, a);
   }
+  prof_end(K_REPLAY, s);
   return hipGetLastError();
 }
 
@@ -285,13 +289,17 @@ static unsigned stream_grid(size_t n) {
 
 hipError_t launch_zero_fill(float* p, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  prof_begin(K_ZERO_FILL, s);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(stream_grid(n)), dim3(256), 0, s, p, n);
+  prof_end(K_ZERO_FILL, s);
   return hipGetLastError();
 }
 
 hipError_t launch_copy(const float* src, float* dst, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  prof_begin(K_COPY, s);
   hipLaunchKernelGGL(copy_kernel, dim3(stream_grid(n)), dim3(256), 0, s, src, dst, n);
+  prof_end(K_COPY, s);
   return hipGetLastError();
 }
 

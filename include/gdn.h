@@ -176,6 +176,18 @@ gdn_status gdn_replay_state_updates(int32_t B, int32_t Hq, int32_t Hv, int32_t d
 gdn_status gdn_state_snapshot(const float* src, float* dst, int64_t num_states, int32_t Hv,
                               int32_t dk, int32_t dv, void* stream);
 
+/*
+ * Measurement support (not part of the method).  gdn_profile_enable(1) makes
+ * every entry point bracket each kernel it launches with a pair of hipEvents
+ * recorded on the launch stream; gdn_profile_collect() waits for all pending
+ * events, reports per kernel the number of launches and their summed duration
+ * in milliseconds (up to max_kernels entries; names are static strings), and
+ * clears the record.  Returns the number of distinct kernels seen.  Disabled by
+ * default; costs nothing measurable when disabled.
+ */
+gdn_status gdn_profile_enable(int32_t on);
+int32_t gdn_profile_collect(const char** names, double* total_ms, int32_t* launches, int32_t max_kernels);
+
 /* Static description of a status code. */
 const char* gdn_status_string(gdn_status status);
 

@@ -102,11 +102,11 @@ def test_workspace_validation_and_sizing(lib):
     sh = shape()
     need = gdn.gdn_prefill_workspace_bytes(sh, 64, False)
     # dense: ceil(64/64)*B chunks fit in the bound (B*T/C + B + 1) * Hv blocks
-    assert need > 0 and need >= (2 + 2 + 1) * 4 * (64 * 64 * 2 * 2 + 512)
+    assert need > 0 and need >= (2 + 2 + 1) * 4 * (2 * 6 * 512 * 2 + 512)
     assert gdn.gdn_prefill_workspace_bytes(sh, 48, False) == 0
     assert gdn.gdn_prefill_workspace_bytes(shape(dk=96), 64, False) == 0
     rag = gdn.gdn_prefill_workspace_bytes(shape(B=4, T=14286, Hq=16, Hv=32), 64, True)
-    assert rag == 256 + (14286 // 64 + 4 + 1) * 32 * (64 * 64 * 2 * 2 + 512)
+    assert rag == 256 + (14286 // 64 + 4 + 1) * 32 * (2 * 6 * 512 * 2 + 512)
     assert prefill(lib, sh, ws=NULL, wsb=0) == gdn.GDN_ERR_INVALID_ARG and "workspace" in last(lib)
     assert prefill(lib, sh, ws=ctypes.c_void_p(0x40000008), wsb=need) == gdn.GDN_ERR_INVALID_ARG
 
