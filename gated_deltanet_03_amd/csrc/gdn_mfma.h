@@ -136,15 +136,11 @@ __device__ __forceinline__ Frag<T> zero_frag() {
   return f;
 }
 
-// The B fragment of the 16 x 16 identity restricted to the lo tile of a block:
-// slot 8g + j (j < 4) holds I[4g + j][n] = (4g + j == n); the hi half is zero.
+// One 16-byte read of 8 consecutive elements as a fragment.
 template <typename T>
-__device__ __forceinline__ Frag<T> identity_frag(int lane) {
-  const int n = lane & 15, g = lane >> 4;
-  f32x4 lo;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lo[j] = (4 * g + j == n) ? 1.f : 0.f;
-  return make_frag<T>(lo, f32x4{0.f, 0.f, 0.f, 0.f});
+__device__ __forceinline__ Frag<T> load_frag_8(const T* p) {
+  return load_frag_native<T>(p);
 }
+
 
 }  // namespace gdn

@@ -350,21 +350,49 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. state pass: grid (slices of 64 columns, Hv, B), 256 threads (4 waves x 16
-//    columns).  Chunk inputs are staged with direct global->LDS loads
-//    (global_load_lds_dwordx4: each wave instruction writes 64 lanes x 16 bytes
-//    contiguously at a wave-uniform LDS address), double-buffered so that chunk
-//    c+1 streams in while chunk c computes.  Row-major tiles are XOR-swizzled
-//    per 16-byte piece (piece p of row r lives at piece p ^ (r mod pieces-per-row))
-//    so that MFMA fragment reads of 16 consecutive rows hit distinct banks.
-//    Rows past a sequence's end are loaded from its last row instead of being
-//    zeroed: A' and MP carry exact zeros in those rows and columns, so the
-//    finite stand-in values never reach an output.
+// 3. state pass: grid (slices of 64 columns, Hv, B), 512 threads = 8 waves.
+//
+//    Each 16-column group of the slice is served by two waves that share a
+//    SIMD: a chain wave (waves 0-3) owning the fp32 state of those columns and
+//    running the sequential part, K*S -> X -> A'*X -> S update; and an output
+//    wave (waves 4-7) running everything off that path: Q*S, the K^T fragments,
+//    MP*Delta and the o stores.  The state crosses over as bf16/f16 fragments
+//    (written by the chain wave after each update), Delta goes the other way.
+//
+//    Chunk inputs are staged with direct global->LDS loads (one wave
+//    instruction writes 64 lanes x 16 bytes contiguously at a wave-uniform LDS
+//    address), double-buffered so chunk c+1 streams in while chunk c computes.
+//    Row-major tiles are XOR-swizzled per 16-byte piece (piece p of row r lives
+//    at piece p ^ (r mod pieces-per-row)) so fragment reads of 16 consecutive
+//    rows hit distinct banks.  Rows past a sequence's end are loaded from its
+//    last row instead of being zeroed: A' and MP carry exact zeros in those rows
+//    and columns, so the finite stand-in values never reach an output.
+//
+//    Per chunk: barrier TOP (chunk c landed; buffers of chunk c-1 free),
+//    chain: KS, X, Delta -> exchange; output: QS, K^T -> LDS; barrier MID;
+//    chain: S update, next state fragments -> exchange; output: O, stores.
 // ---------------------------------------------------------------------------
 // One wave instruction: every lane copies 16 bytes from its src to
 // lds + 16 * lane (lds must be wave-uniform).
 __device__ __forceinline__ void dma16(const void* src, unsigned char* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// The state is carried with its dk rows permuted inside each 32-row block:
+// state row 32kb + 16h + 4g + j holds dk index 32kb + 8g + 4h + j.  A lane's 8
+// contraction slots of a K or Q fragment (rows 4g..4g+3 of the lo and hi tile of
+// the block, the order an accumulator hands them over) then map to 8
+// consecutive dk entries: one 16-byte read.  K * S is unchanged because K's
+// columns are read through the same permutation.  A 16-row block (dk = 16)
+// keeps the identity order.
+template <int DK>
+__device__ __forceinline__ int perm_dk(int r) {
+  if constexpr (DK < 32) {
+    return r;
+  } else {
+    const int kb = r >> 5, h = (r >> 4) & 1, g = (r >> 2) & 3, j = r & 3;
+    return 32 * kb + 8 * g + 4 * h + j;
+  }
 }
 
 template <typename T, int DK>
@@ -374,36 +402,44 @@ struct StateSmem {
   static constexpr int PPR = DK / PER;              // pieces per K/Q row
   static constexpr int ROWB = DK * ES;              // bytes per K/Q row
   static constexpr int NST = DK / 16;               // state row tiles
+  static constexpr int NSB = (NST + 1) / 2;         // state fragments (32-row blocks)
   static constexpr int NKT = 2 * NST;               // K^T fragments (dk tile, token block)
+  static constexpr int FB = FRAG * ES;              // bytes per fragment block
   static constexpr int KB = 64 * ROWB;              // K (or Q) tile bytes
   static constexpr int VB = 64 * 64 * ES;           // V tile bytes (up to 64 columns)
-  static constexpr int AB = 2 * NTRI * FRAG * ES;   // A' and MP fragments
+  static constexpr int AB = 2 * NTRI * FB;          // A' and MP fragments
   static constexpr int STAGE = 2 * KB + VB + AB + 512;
-  static constexpr int KTB = NKT * FRAG * ES;
-  static constexpr int NBUF = 2 * STAGE + KTB <= 160 * 1024 ? 2 : 1;
-  static constexpr size_t total = (size_t)NBUF * STAGE + KTB;
+  static constexpr int KTB = NKT * FB;              // K^T fragments
+  static constexpr int SXB = 4 * NSB * FB;          // state fragments, 4 column groups
+  static constexpr int DXB = 4 * 2 * FB;            // Delta fragments, 4 column groups
+  static constexpr int FIXED = KTB + SXB + DXB;
+  static constexpr int NBUF = 2 * STAGE + FIXED <= 160 * 1024 ? 2 : 1;
+  static constexpr size_t total = (size_t)NBUF * STAGE + FIXED;
   // byte offsets inside one stage buffer
   static constexpr int OK_ = 0, OQ = KB, OV = 2 * KB, OA = 2 * KB + VB, OG = 2 * KB + VB + AB;
 };
 
 template <typename T, int DK, int C>
-__global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
   using SM = StateSmem<T, DK>;
   constexpr int nrt = C / 16;
-  constexpr int NST = SM::NST, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
-  constexpr int NSB = (NST + 1) / 2;      // 32-wide blocks of the dk contraction
+  constexpr int NST = SM::NST, NSB = SM::NSB, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
   constexpr int RPI_K = 64 / PPR;         // K rows per DMA instruction
   constexpr int NA = SM::AB / 1024;       // DMA instructions for A' and MP
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  unsigned char* KTbytes = smem_raw + SM::NBUF * SM::STAGE;
-  T* KT = reinterpret_cast<T*>(KTbytes);
+  unsigned char* fixed = smem_raw + SM::NBUF * SM::STAGE;
+  T* KT = reinterpret_cast<T*>(fixed);
+  T* SX = reinterpret_cast<T*>(fixed + SM::KTB);
+  T* DX = reinterpret_cast<T*>(fixed + SM::KTB + SM::SXB);
 
   const int slice = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const bool chain = wave < 4;
+  const int wq = wave & 3;                                      // column group
   const int ncols = min(64, p.dv - 64 * slice);
-  const int col0 = 64 * slice + 16 * wave;
-  const bool active = 16 * wave < ncols;   // slices narrower than 64 columns idle some waves
+  const int col0 = 64 * slice + 16 * wq;
+  const bool active = 16 * wq < ncols;    // slices narrower than 64 columns idle some groups
   const int i16 = lane & 15, g4 = lane >> 4;
   const int hk = h / (p.Hv / p.Hq);
   const int dv = p.dv;
@@ -421,14 +457,12 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs p) {
   const T* vp = static_cast<const T*>(p.v);
   T* op = static_cast<T*>(p.o);
 
-  // ---- this wave's DMA slots (compile-time counts, loop-invariant offsets) ----
-  // K and Q: PPR instructions each (RPI_K rows per 1 KB), V: pprv instructions,
-  // A'/MP: NA instructions, gamma/tail: half an instruction (wave 3).
+  // ---- DMA slots of chain wave wq (compile-time counts, loop-invariant offsets)
   constexpr int KPW = (PPR + 3) / 4, VPW = (64 / PER + 3) / 4, APW = (NA + 3) / 4;
   int krow[KPW], koff[KPW], vrow[VPW], voff[VPW];
 #pragma unroll
   for (int m = 0; m < KPW; ++m) {
-    const int j = wave + 4 * m;
+    const int j = wq + 4 * m;
     const int r = RPI_K * j + lane / PPR;
     const int pp = (lane % PPR) ^ (r % PPR);           // logical piece stored at this slot
     krow[m] = r;
@@ -436,7 +470,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs p) {
   }
 #pragma unroll
   for (int m = 0; m < VPW; ++m) {
-    const int j = wave + 4 * m;
+    const int j = wq + 4 * m;
     const int r = rpiv * j + lane / pprv;
     const int pp = (lane % pprv) ^ (r % pprv);
     vrow[m] = r;
@@ -454,7 +488,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs p) {
     Block<T> blk(p.chunk_data, (size_t)(cbeg + c), p.Hv, h);
 #pragma unroll
     for (int m = 0; m < KPW; ++m) {
-      const int j = wave + 4 * m;
+      const int j = wq + 4 * m;
       if (j < PPR) {
         const int off = full ? koff[m] : koff[m] + (min(krow[m], last) - krow[m]) * kq_row_stride;
         dma16(kc + off, sb + SM::OK_ + j * 1024);
@@ -463,7 +497,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs p) {
     }
 #pragma unroll
     for (int m = 0; m < VPW; ++m) {
-      const int j = wave + 4 * m;
+      const int j = wq + 4 * m;
       if (j < pprv) {
         const int off = full ? voff[m] : voff[m] + (min(vrow[m], last) - vrow[m]) * v_row_stride;
         dma16(vc + off, sb + SM::OV + j * 1024);
@@ -471,187 +505,239 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs p) {
     }
 #pragma unroll
     for (int m = 0; m < APW; ++m) {
-      const int j = wave + 4 * m;
+      const int j = wq + 4 * m;
       if (j < NA) dma16(blk.A + (j * 64 + lane) * PER, sb + SM::OA + j * 1024);
     }
-    if (wave == 3 && lane < 32) dma16(blk.gam + 4 * lane, sb + SM::OG);
+    if (wq == 3 && lane < 32) dma16(blk.gam + 4 * lane, sb + SM::OG);
   };
 
-  // State tiles: tile r holds rows 16r + 4g + q of column col0 + i16.
+  // fragment (row r, 32-wide dk block kb) of a swizzled K/Q tile: for dk >= 32
+  // the 8 slots of group g are dk 32kb + 8g .. +7 (see perm_dk)
+  auto kq_frag = [&](const unsigned char* tile, int r, int kb) {
+    if constexpr (DK >= 32) {
+      const int piece = (32 * kb + 8 * g4) * ES / 16;
+      if constexpr (ES == 2) {
+        return load_frag_8<T>(reinterpret_cast<const T*>(tile + r * SM::ROWB + ((piece ^ (r % PPR)) << 4)));
+      } else {
+        // fp32: 8 elements span two pieces
+        const T* a = reinterpret_cast<const T*>(tile + r * SM::ROWB + ((piece ^ (r % PPR)) << 4));
+        const T* b = reinterpret_cast<const T*>(tile + r * SM::ROWB + (((piece + 1) ^ (r % PPR)) << 4));
+        return load_frag_rows<T>(a, b);
+      }
+    } else {
+      const int b = 4 * g4 * ES;
+      const T* a = reinterpret_cast<const T*>(tile + r * SM::ROWB + ((((b >> 4) ^ (r % PPR))) << 4) + (b & 15));
+      Frag<T> f = load_frag_rows<T>(a, a);
+      if constexpr (ES == 2) {
+#pragma unroll
+        for (int j = 4; j < 8; ++j) f.v[j] = 0;
+      }
+      return f;
+    }
+  };
+
+
+  // State tiles (chain waves): tile r holds rows 16r + 4g + q of column col0 + i16.
   f32x4 S[NST];
-  if (p.s0 != nullptr && active) {
-    const float* s0 = p.s0 + (int64_t)s * p.s0_stride + ((size_t)h * DK) * dv + col0 + i16;
 #pragma unroll
-    for (int r = 0; r < NST; ++r)
+  for (int r = 0; r < NST; ++r) S[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  T* sx_mine = SX + (wq * NSB * 64 + lane) * 8;   // + kb * 64 * 8
+  T* dx_mine = DX + (wq * 2 * 64 + lane) * 8;     // + blk * 64 * 8
+  if (chain) {
+    if (p.s0 != nullptr && active) {
+      const float* s0 = p.s0 + (int64_t)s * p.s0_stride + ((size_t)h * DK) * dv + col0 + i16;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) S[r][q] = s0[(size_t)(16 * r + 4 * g4 + q) * dv];
-  } else {
+      for (int r = 0; r < NST; ++r)
 #pragma unroll
-    for (int r = 0; r < NST; ++r) S[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q) S[r][q] = s0[(size_t)perm_dk<DK>(16 * r + 4 * g4 + q) * dv];
+    }
+#pragma unroll
+    for (int kb = 0; kb < NSB; ++kb)
+      store_frag_native<T>(sx_mine + kb * 512,
+                           make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f}));
+    if (nch > 0) issue(0, 0);
   }
 
-  const Frag<T> ident = identity_frag<T>(lane);
-  // this lane's o offset inside a chunk: token 4g + q (+16r), column col0 + i16
   const size_t ostride = (size_t)p.Hv * dv;
   const size_t olane = (size_t)(4 * g4) * ostride + (size_t)h * dv + col0 + i16;
-  if (nch > 0) issue(0, 0);
 
   for (int c = 0; c < nch; ++c) {
     const int buf = SM::NBUF == 2 ? (c & 1) : 0;
     const int t0 = st0 + c * C;
     const int len = min(C, st1 - t0);
-    // chunk c has landed in LDS for every wave; every wave is done with chunk c-1
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
+    // chunk c has landed (chain waves issued every DMA); chunk c-1 buffers are free
+    if (chain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
     const unsigned char* sb = smem_raw + buf * SM::STAGE;
-    const T* Ks = reinterpret_cast<const T*>(sb + SM::OK_);
-    const T* Qs = reinterpret_cast<const T*>(sb + SM::OQ);
-    const T* Vs = reinterpret_cast<const T*>(sb + SM::OV);
+    const unsigned char* Kt = sb + SM::OK_;
+    const unsigned char* Qt = sb + SM::OQ;
+    const unsigned char* Vs = sb + SM::OV;
     const T* AMP = reinterpret_cast<const T*>(sb + SM::OA);
     const float* GT = reinterpret_cast<const float*>(sb + SM::OG);
-    // element e of K/Q row r (e a multiple of 4): swizzled piece address
-    auto rowp = [&](const T* tile, int r, int e) {
-      const int b = e * ES;
-      return reinterpret_cast<const T*>(reinterpret_cast<const unsigned char*>(tile) + r * SM::ROWB +
-                                        ((((b >> 4) ^ (r % PPR))) << 4) + (b & 15));
-    };
-
-    // ---- K^T fragments by identity products, shared through LDS -------------
-    //      fragment (dk tile rt, token block kb): lo = K[32kb + 4g + j][16rt + n],
-    //      hi = K[32kb + 16 + 4g + j][16rt + n], i.e. tiles D(t, rt) of K * I.
+    f32x4 QSa[4];
+    Frag<T> Tb0, Tb1;
+    if (chain) {
+      if (SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
+      // ---- KS = K S ------------------------------------------------------------
+      Frag<T> Sb[NSB];
 #pragma unroll
-    for (int f0 = 0; f0 < SM::NKT; f0 += 4) {
-      const int f = f0 + wave;
-      if (f < SM::NKT) {
-        const int rt = f >> 1, kb = f & 1;
-        f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-        if (2 * kb < nrt) {
-          const T* a = rowp(Ks, 32 * kb + i16, 16 * rt + 4 * g4);
-          Frag<T> fa = load_frag_rows<T>(a, a);
-          if constexpr (sizeof(T) == 2) {
+      for (int kb = 0; kb < NSB; ++kb)
+        Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 KSa[4];
 #pragma unroll
-            for (int j = 4; j < 8; ++j) fa.v[j] = 0;
-          }
-          mma_lo<T>(lo, fa, ident);
-        }
-        if (2 * kb + 1 < nrt) {
-          const T* a = rowp(Ks, 32 * kb + 16 + i16, 16 * rt + 4 * g4);
-          Frag<T> fa = load_frag_rows<T>(a, a);
-          if constexpr (sizeof(T) == 2) {
+      for (int r = 0; r < 4; ++r) KSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 4; j < 8; ++j) fa.v[j] = 0;
-          }
-          mma_lo<T>(hi, fa, ident);
-        }
-        store_frag_native<T>(KT + (f * 64 + lane) * 8, make_frag<T>(lo, hi));
+      for (int kb = 0; kb < NSB; ++kb) {
+        Frag<T> ak[nrt];
+#pragma unroll
+        for (int r = 0; r < nrt; ++r) ak[r] = kq_frag(Kt, 16 * r + i16, kb);
+#pragma unroll
+        for (int r = 0; r < nrt; ++r) mma<T>(KSa[r], ak[r], Sb[kb]);
       }
-    }
-
-    // ---- B fragments of the state -------------------------------------------
-    Frag<T> Sb[NSB];
-#pragma unroll
-    for (int kb = 0; kb < NSB; ++kb)
-      Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
-    // ---- KS = K S and QS = Q S: all row tiles advance together per k-block ---
-    f32x4 KSa[4], QSa[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      KSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      QSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kb = 0; kb < NSB; ++kb) {
-      const int hoff = 2 * kb + 1 < NST ? 32 * kb + 16 : 32 * kb;
+      // ---- X = V - gamma * KS ------------------------------------------------
+      f32x4 X[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        X[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (r < nrt) {
-          const int row = 16 * r + i16;
-          mma<T>(KSa[r], load_frag_rows<T>(rowp(Ks, row, 32 * kb + 4 * g4), rowp(Ks, row, hoff + 4 * g4)), Sb[kb]);
-          mma<T>(QSa[r], load_frag_rows<T>(rowp(Qs, row, 32 * kb + 4 * g4), rowp(Qs, row, hoff + 4 * g4)), Sb[kb]);
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+          const int cb = (16 * wq + i16) * ES;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int tok = 16 * r + 4 * g4 + q;
+            const T* vv = reinterpret_cast<const T*>(Vs + tok * rowbv + ((((cb >> 4) ^ (tok & (pprv - 1)))) << 4) +
+                                                     (cb & 15));
+            X[r][q] = Elem<T>::to_f(*vv) - gm[q] * KSa[r][q];
+          }
+        }
+      }
+      const Frag<T> Xb0 = make_frag<T>(X[0], X[1]), Xb1 = make_frag<T>(X[2], X[3]);
+      // ---- Delta = A' X --------------------------------------------------------
+      f32x4 D[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        D[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (r < nrt) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8), Xb0);
+      }
+#pragma unroll
+      for (int r = 2; r < nrt; ++r) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8), Xb1);
+      store_frag_native<T>(dx_mine, make_frag<T>(D[0], D[1]));
+      store_frag_native<T>(dx_mine + 512, make_frag<T>(D[2], D[3]));
+      // ---- tail-weighted Delta for the state update ---------------------------
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 tl = *reinterpret_cast<const f32x4*>(GT + 64 + 16 * r + 4 * g4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) D[r][q] *= tl[q];
+      }
+      Tb0 = make_frag<T>(D[0], D[1]);
+      Tb1 = make_frag<T>(D[2], D[3]);
+    } else {
+      // ---- QS = Q S (state fragments from the chain wave) ----------------------
+#pragma unroll
+      for (int r = 0; r < 4; ++r) QSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NSB; ++kb) {
+        const Frag<T> sbf = load_frag_native<T>(sx_mine + kb * 512);
+        Frag<T> aq[nrt];
+#pragma unroll
+        for (int r = 0; r < nrt; ++r) aq[r] = kq_frag(Qt, 16 * r + i16, kb);
+#pragma unroll
+        for (int r = 0; r < nrt; ++r) mma<T>(QSa[r], aq[r], sbf);
+      }
+      // ---- K^T fragments: fragment (state tile rt, token block kb) holds, for
+      //      state row 16rt + n, K[32kb + 4g + j][dk(16rt + n)] (lo) and the same
+      //      16 tokens later (hi): tiles D(2kb, rt), D(2kb+1, rt) of K * P, P the
+      //      0/1 matrix picking dk column perm_dk(16rt + n) -------------------------
+#pragma unroll
+      for (int f0 = 0; f0 < SM::NKT; f0 += 4) {
+        const int f = f0 + wq;
+        if (f < SM::NKT) {
+          const int rt = f >> 1, kb = f & 1;
+          // B fragment of P: slot 8g + j of the 32-block holding this tile
+          f32x4 plo, phi;
+          if constexpr (DK >= 32) {
+            const int tgt = perm_dk<DK>(16 * rt + i16) - 32 * (rt >> 1);   // dk inside the block
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              plo[j] = (8 * g4 + j == tgt) ? 1.f : 0.f;
+              phi[j] = (8 * g4 + 4 + j == tgt) ? 1.f : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              plo[j] = (4 * g4 + j == i16) ? 1.f : 0.f;
+              phi[j] = 0.f;
+            }
+          }
+          const Frag<T> pf = make_frag<T>(plo, phi);
+          f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+          if (2 * kb < nrt) mma<T>(lo, kq_frag(Kt, 32 * kb + i16, rt >> 1), pf);
+          if (2 * kb + 1 < nrt) mma<T>(hi, kq_frag(Kt, 32 * kb + 16 + i16, rt >> 1), pf);
+          store_frag_native<T>(KT + (f * 64 + lane) * 8, make_frag<T>(lo, hi));
         }
       }
     }
-    // ---- X = V - gamma * KS ---------------------------------------------------
-    f32x4 X[4];
+    lds_barrier();   // MID: Delta and K^T fragments are in LDS; state fragments consumed
+    if (chain) {
+      if (SM::NBUF == 1 && c + 1 < nch) issue(c + 1, 0);
+      // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
+      const float gl = GT[C - 1];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      X[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (r < nrt) {
+      for (int r = 0; r < NST; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) S[r][q] *= gl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (2 * kb < nrt) {
+#pragma unroll
+          for (int r = 0; r < NST; ++r)
+            mma<T>(S[r], load_frag_native<T>(KT + ((2 * r + kb) * 64 + lane) * 8), kb == 0 ? Tb0 : Tb1);
+        }
+      }
+      // next chunk's state fragments for the output wave
+#pragma unroll
+      for (int kb = 0; kb < NSB; ++kb)
+        store_frag_native<T>(sx_mine + kb * 512,
+                             make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f}));
+    } else {
+      // ---- O = scale (gamma QS + MP Delta) -> o -----------------------------------
+      const Frag<T> Db0 = load_frag_native<T>(dx_mine), Db1 = load_frag_native<T>(dx_mine + 512);
+      f32x4 O[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
         const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
-        const int cb = (16 * wave + i16) * ES;          // byte of this column inside a V row
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int tok = 16 * r + 4 * g4 + q;
-          const T* vv = reinterpret_cast<const T*>(reinterpret_cast<const unsigned char*>(Vs) + tok * rowbv +
-                                                   ((((cb >> 4) ^ (tok & (pprv - 1)))) << 4) + (cb & 15));
-          X[r][q] = Elem<T>::to_f(*vv) - gm[q] * KSa[r][q];
-        }
+        for (int q = 0; q < 4; ++q) O[r][q] = gm[q] * QSa[r][q];
+        if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 0)) * 64 + lane) * 8), Db0);
       }
-    }
-    const Frag<T> Xb0 = make_frag<T>(X[0], X[1]), Xb1 = make_frag<T>(X[2], X[3]);
-    // ---- Delta = A' X ---------------------------------------------------------
-    f32x4 D[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      D[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (r < nrt) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8), Xb0);
-    }
+      for (int r = 2; r < nrt; ++r)
+        mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 1)) * 64 + lane) * 8), Db1);
+      if (active) {
+        T* oc = op + (size_t)t0 * ostride + olane;
+        if (len == C) {
 #pragma unroll
-    for (int r = 2; r < 4; ++r)
-      if (r < nrt) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8), Xb1);
-    const Frag<T> Db0 = make_frag<T>(D[0], D[1]), Db1 = make_frag<T>(D[2], D[3]);
-    // ---- O = scale (gamma QS + MP Delta) -> o ----------------------------------
-    f32x4 O[4];
+          for (int r = 0; r < nrt; ++r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+            for (int q = 0; q < 4; ++q) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
+        } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) O[r][q] = gm[q] * QSa[r][q];
-      if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 0)) * 64 + lane) * 8), Db0);
-    }
+          for (int r = 0; r < nrt; ++r)
 #pragma unroll
-    for (int r = 2; r < 4; ++r)
-      if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 1)) * 64 + lane) * 8), Db1);
-    if (active) {
-      T* oc = op + (size_t)t0 * ostride + olane;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (16 * r + 4 * g4 + q < len) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
-    }
-    // ---- tail-weighted Delta ---------------------------------------------------
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 tl = *reinterpret_cast<const f32x4*>(GT + 64 + 16 * r + 4 * g4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) D[r][q] *= tl[q];
-    }
-    const Frag<T> Tb0 = make_frag<T>(D[0], D[1]), Tb1 = make_frag<T>(D[2], D[3]);
-    const float gl = GT[C - 1];
-    lds_barrier();   // K^T fragments of every wave are in LDS; stage reads are done
-    if (SM::NBUF == 1 && c + 1 < nch) issue(c + 1, 0);
-    // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
-#pragma unroll
-    for (int r = 0; r < NST; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) S[r][q] *= gl;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (2 * kb < nrt) {
-#pragma unroll
-        for (int r = 0; r < NST; ++r)
-          mma<T>(S[r], load_frag_native<T>(KT + ((2 * r + kb) * 64 + lane) * 8), kb == 0 ? Tb0 : Tb1);
+            for (int q = 0; q < 4; ++q)
+              if (16 * r + 4 * g4 + q < len) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
+        }
       }
     }
   }
 
-  if (p.s_out != nullptr && active) {
+  if (chain && p.s_out != nullptr && active) {
     float* so = p.s_out + ((size_t)s * p.Hv + h) * DK * dv + col0 + i16;
 #pragma unroll
     for (int r = 0; r < NST; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) so[(size_t)(16 * r + 4 * g4 + q) * dv] = S[r][q];
+      for (int q = 0; q < 4; ++q) so[(size_t)perm_dk<DK>(16 * r + 4 * g4 + q) * dv] = S[r][q];
   }
 }
 
@@ -678,6 +764,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   }
   const int nslices = (a.dv + 63) / 64;
   const size_t sm2 = StateSmem<T, DK>::total;
+  if (sm2 > 160 * 1024) return hipErrorInvalidValue;
   static bool attr2 = false;
   if (!attr2) {
     e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -686,7 +773,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     attr2 = true;
   }
   prof_begin(K_STATE, st);
-  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C>), dim3(nslices, a.Hv, a.B), dim3(256), sm2, st, a);
+  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C>), dim3(nslices, a.Hv, a.B), dim3(512), sm2, st, a);
   prof_end(K_STATE, st);
   return hipGetLastError();
 }

@@ -69,6 +69,7 @@ def test_shape_validation(lib):
     assert step(lib, shape(B=-1)) == gdn.GDN_ERR_INVALID_ARG
     assert step(lib, shape(scale=float("nan"))) == gdn.GDN_ERR_INVALID_ARG
     assert prefill(lib, shape(), chunk=48) == gdn.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, shape(dtype=gdn.GDN_F32, dk=128)) == gdn.GDN_ERR_UNSUPPORTED
 
 
 def test_pointer_validation(lib):
