@@ -25,6 +25,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           # keep MFMA accumulators in VGPRs (no AGPR round trips around VALU work)
           "-mllvm", "-amdgpu-mfma-vgpr-form",
+          # the register-resident substitution and fragment loops rely on full unrolling
+          "-mllvm", "-pragma-unroll-threshold=1000000",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

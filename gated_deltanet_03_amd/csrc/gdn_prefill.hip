@@ -109,147 +109,109 @@ struct Block {  // views of one (chunk, value head) workspace block
 };
 
 // ---------------------------------------------------------------------------
-// 2. chunk prep: grid (max_chunks, Hq), 256 threads
+// 2. chunk prep: one wave per (chunk, value head), 1-D grid.
+//
+//    K and Q fragments are read straight from global memory (8 consecutive dk
+//    entries = one 16-byte load per lane) and the Gram products K K^T and K Q^T
+//    run on MFMA with fp32 accumulation.  MP fragments come straight out of the
+//    K Q^T accumulators: lane (g, n) of tile (c, r) of K Q^T holds
+//    P[16r + n][16c + 4g + q], which is the A fragment of block (r, c) of Q K^T.
+//
+//    UT inverse X = (I + L)^-1 by 16 x 16 blocks, all in fp32:
+//      * diagonal blocks X_jj = (I + L_jj)^-1: back-substitution on the VALU,
+//        lane (b, r) computing row r of block b (the only LDS traffic);
+//      * off-diagonal blocks from X N = I, N = I + L:
+//          X_ij = -(sum_{k=j+1..i} X_ik L_kj) X_jj,
+//        carried transposed, Z_ij = X_ij^T = -Z_jj sum_k L_kj^T Z_ik, on fp32
+//        MFMA with every operand already in accumulator layout (an accumulator
+//        tile E is the A operand of E^T and the B operand of E).
+//    Lane (g, n) of Z_ij holds X[16i + n][16j + 4g + q], so A' = X diag(beta)
+//    is written in fragment order straight from the Z tiles.
+//    Rows past a sequence's end see zero keys, queries and beta, so their L and
+//    MP entries vanish and their rows/columns of A' are exactly zero.
 // ---------------------------------------------------------------------------
-constexpr int FS = 68;  // fp32 64x64 matrix row stride in LDS (16-byte aligned rows)
+constexpr int DS = 20;   // row stride (floats) of the 16 x 16 diagonal blocks in LDS
 
+// Fragment of K or Q row `row` (a pointer to its first element), 32-wide dk
+// block kb, in the contiguous slot order of the state kernel (slots 8g..8g+7 =
+// dk 32kb + 8g .. +7); dk = 16 puts dk 4g..4g+3 in the lo half, zero in the hi.
 template <typename T, int DK>
-struct PrepSmem {
-  static constexpr int KS = DK + 16 / (int)sizeof(T);  // padded K/Q rows (16-byte aligned)
-  static constexpr size_t mat = 64 * FS * 4;
-  static constexpr size_t kq = 2 * 64 * KS * sizeof(T);
-  // region A: Ks, Qs during the Gram products, then Lm and Ai
-  static constexpr size_t regA = kq > 2 * mat ? kq : 2 * mat;
-  // region B: KK and P; P is later reused as Tm
-  static constexpr size_t regB = 2 * mat;
-  static size_t total(int G) { return regA + regB + (size_t)G * 2 * 64 * 4; }
-};
-
-// One doubling level of the blocked inverse: for each pair of BS x BS diagonal
-// blocks (lo, hi) already inverted, A[hi, lo] = -A[hi,hi] L[hi,lo] A[lo,lo].
-template <int BS>
-__device__ __forceinline__ void inverse_level(const float* Lm, float* Ai, float* Tm, int npairs, int tid) {
-  constexpr int CPT = BS == 16 ? 2 : 4;    // output columns per thread
-  constexpr int CG = BS / CPT;
-  constexpr int PER = BS * CG;             // jobs per pair
-  for (int job = tid; job < npairs * PER; job += 256) {
-    const int pr = job / PER, rem = job % PER;
-    const int i = rem / CG, c = (rem % CG) * CPT;
-    const int r0 = (2 * pr + 1) * BS, c0 = 2 * pr * BS;
-    float acc[CPT];
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) acc[u] = 0.f;
-#pragma unroll
-    for (int k = 0; k < BS; ++k) {
-      const float l = Lm[(r0 + i) * FS + c0 + k];
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) acc[u] = fmaf(l, Ai[(c0 + k) * FS + c0 + c + u], acc[u]);
+__device__ __forceinline__ Frag<T> gload_frag(const T* __restrict__ row, int kb, int g4, bool valid) {
+  Frag<T> f = zero_frag<T>();
+  if (!valid) return f;
+  if constexpr (DK >= 32) {
+    f = load_frag_native<T>(row + 32 * kb + 8 * g4);
+  } else {
+    if constexpr (sizeof(T) == 4) {
+      f.lo = *reinterpret_cast<const f32x4*>(row + 4 * g4);
+    } else {
+      const auto a = *reinterpret_cast<const typename Half4<T>::type*>(row + 4 * g4);
+      f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
     }
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) Tm[(r0 + i) * FS + c0 + c + u] = acc[u];
   }
-  lds_barrier();
-  for (int job = tid; job < npairs * PER; job += 256) {
-    const int pr = job / PER, rem = job % PER;
-    const int i = rem / CG, c = (rem % CG) * CPT;
-    const int r0 = (2 * pr + 1) * BS, c0 = 2 * pr * BS;
-    float acc[CPT];
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) acc[u] = 0.f;
-#pragma unroll
-    for (int k = 0; k < BS; ++k) {
-      const float a = Ai[(r0 + i) * FS + r0 + k];
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) acc[u] = fmaf(a, Tm[(r0 + k) * FS + c0 + c + u], acc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) Ai[(r0 + i) * FS + c0 + c + u] = -acc[u];
-  }
-  lds_barrier();
+  return f;
 }
 
-template <typename T, int DK, int C>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
-  using SM = PrepSmem<T, DK>;
-  constexpr int KS = SM::KS;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* Ks = reinterpret_cast<T*>(smem_raw);
-  T* Qs = Ks + 64 * KS;
-  float* Lm = reinterpret_cast<float*>(smem_raw);
-  float* Ai = Lm + 64 * FS;
-  float* KK = reinterpret_cast<float*>(smem_raw + SM::regA);
-  float* P = KK + 64 * FS;
-  float* Tm = P;
-  const int G = p.Hv / p.Hq;
-  float* Gs = P + 64 * FS;   // [G][64]
-  float* Bs = Gs + G * 64;   // [G][64]
+template <typename T, int DK>
+__device__ __forceinline__ void gram_mma(f32x4& acc, const Frag<T>& a, const Frag<T>& b) {
+  if constexpr (DK >= 32) mma<T>(acc, a, b); else mma_lo<T>(acc, a, b);
+}
 
-  const int gc = blockIdx.x, hk = blockIdx.y;
+// acc += E^T F for 16 x 16 fp32 tiles E, F given in accumulator layout (lane
+// (g, n) holds row 4g + q, column n): contraction index 4g + s in step s.
+__device__ __forceinline__ void mma_tn(f32x4& acc, const f32x4& e, const f32x4& f) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(e[s], f[s], acc, 0, 0, 0);
+}
+
+// exp2 on the transcendental unit (1 ulp; results below 2^-126 flush to zero,
+// which only drops terms already below fp32 resolution of the sums they enter).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T, int DK, int C>
+__global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
+  constexpr int nrt = C / 16;
+  constexpr int NKB = DK >= 32 ? DK / 32 : 1;
+  constexpr float LOG2E = 1.4426950408889634f;
+  __shared__ __align__(16) float Ld[4 * 16 * DS];   // diagonal blocks of L
+  __shared__ __align__(16) float Xd[4 * 16 * DS];   // their inverses, row-major
+  __shared__ __align__(16) float Gs[64];            // log2 cumulative decay
+  __shared__ __align__(16) float Bs[64];            // beta
+
+  // XCD-aware order: workgroup w runs on XCD w % 8; give each XCD a contiguous
+  // run of (chunk, head) items so the value heads of one key head share an L2.
+  const int nitems = p.max_chunks * p.Hv;
+  const int per = (nitems + 7) >> 3;
+  const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (item >= nitems) return;
+  const int gc = item / p.Hv, h = item % p.Hv;
   const int nchunks = p.chunk_offsets[p.B];
   if (gc >= nchunks) return;
   const int s = find_seq(p.chunk_offsets, p.B, gc);
   int st0, st1;
   seq_range(p.cu, p.T, p.total, s, st0, st1);
-  constexpr int nrt = C / 16;
   const int t0 = st0 + (gc - p.chunk_offsets[s]) * C;
   const int len = min(C, st1 - t0);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int lane = threadIdx.x;
   const int i16 = lane & 15, g4 = lane >> 4;
+  const int hk = h / (p.Hv / p.Hq);
+  Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
 
-  // ---- load K and Q rows (zero past the chunk end) -------------------------
+  // ---- K fragments of every row tile, Q fragments of row tile 0 -------------
+  const T* kp = static_cast<const T*>(p.k);
+  const T* qp = static_cast<const T*>(p.q);
+  const size_t lane_off = ((size_t)(t0 + i16) * p.Hq + hk) * DK;
+  const size_t tile_step = (size_t)16 * p.Hq * DK;
+  Frag<T> kf[nrt][NKB], qf[NKB];
+#pragma unroll
+  for (int r = 0; r < nrt; ++r)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kf[r][kb] = gload_frag<T, DK>(kp + lane_off + r * tile_step, kb, g4, 16 * r + i16 < len);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) qf[kb] = gload_frag<T, DK>(qp + lane_off, kb, g4, i16 < len);
+
+  // ---- log2 cumulative decay, beta, gamma and tail -------------------------
   {
-    constexpr int PER = 16 / (int)sizeof(T);
-    constexpr int CPR = DK / PER;
-    const T* kp = static_cast<const T*>(p.k);
-    const T* qp = static_cast<const T*>(p.q);
-    for (int id = tid; id < 64 * CPR; id += 256) {
-      const int r = id / CPR, c = (id % CPR) * PER;
-      uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-      if (r < len) {
-        const size_t off = ((size_t)(t0 + r) * p.Hq + hk) * DK + c;
-        kv = *reinterpret_cast<const uint4*>(kp + off);
-        qv = *reinterpret_cast<const uint4*>(qp + off);
-      }
-      *reinterpret_cast<uint4*>(Ks + r * KS + c) = kv;
-      *reinterpret_cast<uint4*>(Qs + r * KS + c) = qv;
-    }
-  }
-  lds_barrier();
-
-  // ---- Gram products on MFMA: KK = K K^T and P = Q K^T, tiles (r, c) r >= c -
-  {
-    const int ntri = nrt * (nrt + 1) / 2;
-    for (int job = wave; job < 2 * ntri; job += 4) {
-      const bool isP = job >= ntri;
-      int t = isP ? job - ntri : job, r = 0;
-      while (t > r) { t -= r + 1; ++r; }
-      const int c = t;
-      const T* arow = (isP ? Qs : Ks) + (16 * r + i16) * KS + 4 * g4;
-      const T* brow = Ks + (16 * c + i16) * KS + 4 * g4;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb)
-        mma<T>(acc, load_frag_rows<T>(arow + 32 * kb, arow + 32 * kb + 16),
-               load_frag_rows<T>(brow + 32 * kb, brow + 32 * kb + 16));
-      if constexpr (DK == 16) {
-        Frag<T> a = load_frag_rows<T>(arow, arow), b = load_frag_rows<T>(brow, brow);
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int j = 4; j < 8; ++j) { a.v[j] = 0; b.v[j] = 0; }
-        }
-        mma_lo<T>(acc, a, b);
-      }
-      float* D = isP ? P : KK;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) D[(16 * r + 4 * g4 + q) * FS + 16 * c + i16] = acc[q];
-    }
-  }
-  lds_barrier();
-
-  // ---- cumulative log decay per value head (one wave per head) -------------
-  for (int v = wave; v < G; v += 4) {
-    const int h = hk * G + v;
     float gv = 0.f, bv = 0.f;
     if (lane < len) {
       gv = p.g[(size_t)(t0 + lane) * p.Hv + h];
@@ -261,91 +223,152 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
       const float y = __shfl_up(x, off);
       if (lane >= off) x += y;
     }
-    Gs[v * 64 + lane] = x;
-    Bs[v * 64 + lane] = bv;
     const float glast = __shfl(x, C - 1);
-    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
+    Gs[lane] = x * LOG2E;
+    Bs[lane] = bv;
     blk.gam[lane] = expf(x);
     blk.tail[lane] = expf(glast - x);
   }
-  lds_barrier();
 
-  // ---- MP fragments for every value head of this key head ------------------
-  for (int job = tid; job < G * NTRI * 64; job += 256) {
-    const int v = job / (NTRI * 64), f = (job / 64) % NTRI, l = job & 63;
+  // ---- MP = exp(G_i - G_j) (Q K^T)_ij, j <= i ------------------------------
+#pragma unroll
+  for (int r = 0; r < nrt; ++r) {
+    Frag<T> qn[NKB];
+    if (r + 1 < nrt) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        qn[kb] = gload_frag<T, DK>(qp + lane_off + (r + 1) * tile_step, kb, g4, 16 * (r + 1) + i16 < len);
+    }
+    f32x4 kq[nrt];
+#pragma unroll
+    for (int c = 0; c <= r; ++c) {
+      kq[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kq[c], kf[c][kb], qf[kb]);
+    }
+    const int i = 16 * r + i16;
+    const float gi = Gs[i];
+#pragma unroll
+    for (int c = 0; c <= r; ++c) {
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[16 * c + 4 * g4]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = 16 * c + 4 * g4 + q;
+        kq[c][q] = j <= i ? fast_exp2(gi - gj[q]) * kq[c][q] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb <= r / 2; ++kb) {
+      const f32x4 hi = 2 * kb + 1 <= r ? kq[2 * kb + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+      store_frag_native<T>(blk.MP + (tri_idx(r, kb) * 64 + lane) * 8, make_frag<T>(kq[2 * kb], hi));
+    }
+    if (r + 1 < nrt) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) qf[kb] = qn[kb];
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < NTRI; ++f) {
     int r, kb;
     tri_rc(f, r, kb);
-    const int row = 16 * r + (l & 15), gg = l >> 4;
-    const float* Gv = Gs + v * 64;
-    float val[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = 32 * kb + (j < 4 ? 4 * gg + j : 16 + 4 * gg + j - 4);
-      val[j] = (col <= row && row < C) ? expf(Gv[row] - Gv[col]) * P[row * FS + col] : 0.f;
-    }
-    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, hk * G + v);
-    store_frag_native<T>(blk.MP + (f * 64 + l) * 8,
-                         make_frag<T>(f32x4{val[0], val[1], val[2], val[3]}, f32x4{val[4], val[5], val[6], val[7]}));
+    if (r >= nrt) store_frag_native<T>(blk.MP + (f * 64 + lane) * 8, zero_frag<T>());
   }
-  lds_barrier();   // P is dead from here on (its space becomes Tm)
 
-  for (int v = 0; v < G; ++v) {
-    const int h = hk * G + v;
-    const float* Gv = Gs + v * 64;
-    const float* Bv = Bs + v * 64;
-    // ---- L (strictly lower, beta-scaled, decay-weighted) and A := 0 ---------
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-      const int i = idx >> 6, j = idx & 63;
-      float l = 0.f;
-      if (j < i && i < C) l = Bv[i] * expf(Gv[i] - Gv[j]) * KK[i * FS + j];
-      Lm[i * FS + j] = l;
-      Ai[i * FS + j] = 0.f;
-    }
-    lds_barrier();
-    // ---- 16x16 diagonal blocks by forward substitution (lane = column) -----
-    if (wave < nrt && lane < 16) {
-      const int b0 = 16 * wave, c = lane;
-      float x[16];
+  // ---- L_ij = beta_i exp(G_i - G_j) (K K^T)_ij, j < i: off-diagonal tiles stay
+  //      in registers, diagonal tiles go to LDS for the substitution ------------
+  f32x4 Lt[nrt][nrt];   // [r][c], c < r used
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        float Lr[16];
+  for (int r = 0; r < nrt; ++r) {
+    const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[16 * r + 4 * g4]);
+    const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[16 * r + 4 * g4]);
 #pragma unroll
-        for (int jj = 0; jj < 16; jj += 4) {
-          const float4 w = *reinterpret_cast<const float4*>(&Lm[(b0 + ii) * FS + b0 + jj]);
-          Lr[jj] = w.x; Lr[jj + 1] = w.y; Lr[jj + 2] = w.z; Lr[jj + 3] = w.w;
-        }
-        float acc = (ii == c) ? 1.f : 0.f;
+    for (int c = 0; c <= r; ++c) {
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jj = 0; jj < ii; ++jj) acc = fmaf(-Lr[jj], x[jj], acc);
-        x[ii] = acc;
+      for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kk, kf[r][kb], kf[c][kb]);
+      const float gj = Gs[16 * c + i16];
+      f32x4 l;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool below = c < r || i16 < 4 * g4 + q;
+        l[q] = below ? bi[q] * fast_exp2(gi[q] - gj) * kk[q] : 0.f;
       }
+      if (c < r) {
+        Lt[r][c] = l;
+      } else {
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) Ai[(b0 + ii) * FS + b0 + c] = x[ii];
-    }
-    lds_barrier();
-    // ---- doubling: 16 -> 32 -> 64 ------------------------------------------
-    if (C >= 32) inverse_level<16>(Lm, Ai, Tm, C / 32, tid);
-    if (C >= 64) inverse_level<32>(Lm, Ai, Tm, 1, tid);
-    // ---- A' = A diag(beta) as fragment-native lower-triangular blocks -------
-    {
-      Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
-      for (int job = tid; job < NTRI * 64; job += 256) {
-        const int f = job / 64, l = job & 63;
-        int r, kb;
-        tri_rc(f, r, kb);
-        const int row = 16 * r + (l & 15), gg = l >> 4;
-        float val[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = 32 * kb + (j < 4 ? 4 * gg + j : 16 + 4 * gg + j - 4);
-          val[j] = (row < C && col < C) ? Ai[row * FS + col] * Bv[col] : 0.f;
-        }
-        store_frag_native<T>(blk.A + (f * 64 + l) * 8,
-                             make_frag<T>(f32x4{val[0], val[1], val[2], val[3]},
-                                          f32x4{val[4], val[5], val[6], val[7]}));
+        for (int q = 0; q < 4; ++q) Ld[(r * 16 + 4 * g4 + q) * DS + i16] = l[q];
       }
     }
-    lds_barrier();
+  }
+
+  // ---- diagonal blocks: lane (b, r) computes row r of (I + L_bb)^-1 by
+  //      back-substitution, X (I + L) = I, over k = 15 .. 1 -------------------
+  {
+    const int b = lane >> 4, r = lane & 15;
+    const float* Lb = Ld + b * 16 * DS;
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = (j == r) ? 1.f : 0.f;
+#pragma unroll
+    for (int k = 15; k >= 1; --k) {
+      const float xk = x[k];
+#pragma unroll
+      for (int j4 = 0; j4 < k; j4 += 4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lb + k * DS + j4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j4 + u < k) x[j4 + u] = fmaf(-l4[u], xk, x[j4 + u]);
+      }
+    }
+    float* xr = Xd + (b * 16 + r) * DS;
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) *reinterpret_cast<f32x4*>(xr + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the whole wave's rows are in LDS
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- off-diagonal blocks, by distance from the diagonal ------------------
+  f32x4 Xa[nrt], Z[nrt][nrt];   // Xa[j]: X_jj in accumulator layout; Z[i][j] = X_ij^T
+#pragma unroll
+  for (int j = 0; j < nrt; ++j) {
+    const float* xb = Xd + j * 16 * DS;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Xa[j][q] = xb[(4 * g4 + q) * DS + i16];
+    Z[j][j] = *reinterpret_cast<const f32x4*>(xb + i16 * DS + 4 * g4);
+  }
+#pragma unroll
+  for (int d = 1; d < nrt; ++d)
+#pragma unroll
+    for (int j = 0; j + d < nrt; ++j) {
+      const int i = j + d;
+      f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = j + 1; k <= i; ++k) mma_tn(P, Lt[k][j], Z[i][k]);
+      f32x4 zij = {0.f, 0.f, 0.f, 0.f};
+      mma_tn(zij, Xa[j], P);
+      Z[i][j] = -zij;
+    }
+
+  // ---- A' = X diag(beta) in fragment order: lane (g, n) of Z[i][j] holds
+  //      X[16i + n][16j + 4g + q] -----------------------------------------------
+#pragma unroll
+  for (int f = 0; f < NTRI; ++f) {
+    int r, kb;
+    tri_rc(f, r, kb);
+    Frag<T> fr = zero_frag<T>();
+    if (r < nrt) {
+      const int c0 = 2 * kb, c1 = 2 * kb + 1;
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&Bs[16 * c0 + 4 * g4]);
+      const f32x4 lo = Z[r][c0] * b0;
+      f32x4 hi = {0.f, 0.f, 0.f, 0.f};
+      if (c1 <= r) {
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&Bs[16 * c1 + 4 * g4]);
+        hi = Z[r][c1] * b1;
+      }
+      fr = make_frag<T>(lo, hi);
+    }
+    store_frag_native<T>(blk.A + (f * 64 + lane) * 8, fr);
   }
 }
 
@@ -752,13 +775,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 0) {
-    const size_t sm1 = PrepSmem<T, DK>::total(a.Hv / a.Hq);
-    if (sm1 > 160 * 1024) return hipErrorInvalidValue;
-    e = hipFuncSetAttribute((const void*)chunk_prep_kernel<T, DK, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sm1);
-    if (e != hipSuccess) return e;
+    const long long items = (long long)a.max_chunks * a.Hv;
+    const long long blocks = 8 * ((items + 7) / 8);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     prof_begin(K_PREP, st);
-    hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C>), dim3(a.max_chunks, a.Hq), dim3(256), sm1, st, a);
+    hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C>), dim3((unsigned)blocks), dim3(64), 0, st, a);
     prof_end(K_PREP, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -794,7 +815,10 @@ static hipError_t launch_prefill_dt(const PrefillArgs& a, hipStream_t st) {
     case 16: return launch_prefill_c<T, 16>(a, st);
     case 32: return launch_prefill_c<T, 32>(a, st);
     case 64: return launch_prefill_c<T, 64>(a, st);
-    case 128: return launch_prefill_c<T, 128>(a, st);
+    case 128:
+      // fp32 with dk = 128 does not fit the state kernel's LDS budget (rejected on the host)
+      if constexpr (sizeof(T) == 4) return hipErrorInvalidValue;
+      else return launch_prefill_c<T, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }
