@@ -55,6 +55,8 @@ gdn_status check_shape(const gdn_shape* sh, const int32_t* cu, int64_t* total_to
     return fail(GDN_ERR_UNSUPPORTED, "dk=%d, dv=%d: supported head dims are 16, 32, 64, 128", sh->dk, sh->dv);
   if (sh->B > 65535 || sh->Hv > 65535)
     return fail(GDN_ERR_UNSUPPORTED, "B=%d or Hv=%d exceeds 65535", sh->B, sh->Hv);
+  if ((int64_t)sh->B * sh->Hv > (1 << 24))
+    return fail(GDN_ERR_UNSUPPORTED, "B*Hv=%lld exceeds 2^24 (row, head) pairs", (long long)sh->B * sh->Hv);
   if (!(sh->scale == sh->scale)) return fail(GDN_ERR_INVALID_ARG, "scale is NaN");
   int64_t total = cu ? (int64_t)sh->T : (int64_t)sh->B * sh->T;
   if (total > (int64_t)0x7fffffff) return fail(GDN_ERR_UNSUPPORTED, "more than 2^31-1 tokens");
@@ -120,16 +122,28 @@ const char* gdn_status_string(gdn_status st) {
 
 const char* gdn_last_error(void) { return g_last_error; }
 
+// Workspace: [chunk_offsets: B+1 int32][pad to 16][chunk_info: max_chunks x
+// (first token, length) int32 pairs][pad to 256][per (chunk, value head) blocks].
+// Upper bound on chunks: every sequence adds at most one partial chunk.
+struct WsLayout {
+  int64_t max_chunks;
+  size_t info_off, head;
+};
+static WsLayout ws_layout(const gdn_shape* sh, int32_t chunk, int64_t total) {
+  WsLayout w;
+  w.max_chunks = total / chunk + sh->B + 1;
+  w.info_off = align_up((size_t)(sh->B + 1) * 4, 16);
+  w.head = align_up(w.info_off + (size_t)w.max_chunks * 8, 256);
+  return w;
+}
+
 size_t gdn_prefill_workspace_bytes(const gdn_shape* sh, int32_t chunk, int32_t ragged) {
   int64_t total = 0;
   static const int32_t dummy = 0;
   if (check_shape(sh, ragged ? &dummy : nullptr, &total) != GDN_OK) return 0;
   if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
-  // Upper bound on chunks: every sequence adds at most one partial chunk.
-  int64_t max_chunks = total / chunk + sh->B + 1;
-  size_t head = align_up((size_t)(sh->B + 1) * 4, 256);
-  size_t blocks = (size_t)max_chunks * sh->Hv * gdn::chunk_block_bytes((gdn::DType)sh->dtype);
-  return head + blocks;
+  const WsLayout w = ws_layout(sh, chunk, total);
+  return w.head + (size_t)w.max_chunks * sh->Hv * gdn::chunk_block_bytes((gdn::DType)sh->dtype);
 }
 
 gdn_status gdn_prefill_chunked(const gdn_shape* sh, const void* q, const void* k, const void* v,
@@ -161,11 +175,13 @@ gdn_status gdn_prefill_chunked(const gdn_shape* sh, const void* q, const void* k
   a.B = sh->B; a.T = sh->T; a.total = (int32_t)total;
   a.Hq = sh->Hq; a.Hv = sh->Hv; a.dk = sh->dk; a.dv = sh->dv; a.scale = sh->scale;
   a.chunk = chunk;
-  size_t head = align_up((size_t)(sh->B + 1) * 4, 256);
-  size_t blk = gdn::chunk_block_bytes((gdn::DType)sh->dtype);
-  a.max_chunks = (int32_t)((need - head) / (blk * sh->Hv));
+  const WsLayout w = ws_layout(sh, chunk, total);
+  if (w.max_chunks * sh->Hv > 0x7fffffffLL - 8)
+    return fail(GDN_ERR_UNSUPPORTED, "too many (chunk, head) pairs (%lld)", (long long)w.max_chunks * sh->Hv);
+  a.max_chunks = (int32_t)w.max_chunks;
   a.chunk_offsets = static_cast<int32_t*>(ws);
-  a.chunk_data = static_cast<char*>(ws) + head;
+  a.chunk_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.info_off);
+  a.chunk_data = static_cast<char*>(ws) + w.head;
   hipError_t e = gdn::launch_prefill((gdn::DType)sh->dtype, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");
   return GDN_OK;
@@ -221,6 +237,7 @@ gdn_status gdn_replay_state_updates(int32_t B, int32_t Hq, int32_t Hv, int32_t d
     return fail(GDN_ERR_UNSUPPORTED, "dk=%d, dv=%d: supported head dims are 16, 32, 64, 128", dk, dv);
   if (cap < 0) return fail(GDN_ERR_INVALID_ARG, "state_update_capacity=%d < 0", cap);
   if (B > 65535 || Hv > 65535) return fail(GDN_ERR_UNSUPPORTED, "B or Hv exceeds 65535");
+  if ((int64_t)B * Hv > (1 << 24)) return fail(GDN_ERR_UNSUPPORTED, "B*Hv exceeds 2^24 (row, head) pairs");
   if (B == 0 || cap == 0) return GDN_OK;
   if (su == nullptr || counts == nullptr || state == nullptr)
     return fail(GDN_ERR_INVALID_ARG, "state_update, replay_count and state are required");

@@ -55,6 +55,7 @@ struct PrefillArgs {
   int32_t chunk;         // 16, 32 or 64
   int32_t max_chunks;    // workspace capacity in chunks
   int32_t* chunk_offsets;   // [B+1] inside the workspace
+  int32_t* chunk_info;      // [max_chunks][2]: first token, length (0 past the last chunk)
   void* chunk_data;         // per (chunk, value head) blocks inside the workspace
 };
 

@@ -81,16 +81,27 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(PrefillArgs p) {
     __syncthreads();
   }
   if (threadIdx.x == 0) p.chunk_offsets[p.B] = carry_s;
-}
-
-// Locate global chunk gc: sequence s with offsets[s] <= gc < offsets[s+1].
-__device__ __forceinline__ int find_seq(const int32_t* off, int B, int gc) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= gc) lo = mid; else hi = mid - 1;
+  __syncthreads();   // the offsets written above are visible to the whole workgroup
+  // per-chunk (first token, length), one thread per chunk: the sequence of
+  // chunk c is the last s with offsets[s] <= c; entries past the last chunk
+  // get length 0
+  const int nch = carry_s;
+  for (int c = threadIdx.x; c < p.max_chunks; c += 256) {
+    int a = 0, n = 0;
+    if (c < nch) {
+      int lo = 0, hi = p.B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.chunk_offsets[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      int t0, t1;
+      seq_range(p.cu, p.T, p.total, lo, t0, t1);
+      a = t0 + (c - p.chunk_offsets[lo]) * p.chunk;
+      n = min(p.chunk, t1 - a);
+    }
+    p.chunk_info[2 * c] = a;
+    p.chunk_info[2 * c + 1] = n;
   }
-  return lo;
 }
 
 template <typename T>
@@ -135,10 +146,11 @@ constexpr int DS = 20;   // row stride (floats) of the 16 x 16 diagonal blocks i
 // Fragment of K or Q row `row` (a pointer to its first element), 32-wide dk
 // block kb, in the contiguous slot order of the state kernel (slots 8g..8g+7 =
 // dk 32kb + 8g .. +7); dk = 16 puts dk 4g..4g+3 in the lo half, zero in the hi.
+// Loads are unconditional (callers clamp the row into the chunk) so a wave's
+// loads issue back to back; rows past the chunk end are zeroed afterwards.
 template <typename T, int DK>
-__device__ __forceinline__ Frag<T> gload_frag(const T* __restrict__ row, int kb, int g4, bool valid) {
+__device__ __forceinline__ Frag<T> gload_frag(const T* __restrict__ row, int kb, int g4) {
   Frag<T> f = zero_frag<T>();
-  if (!valid) return f;
   if constexpr (DK >= 32) {
     f = load_frag_native<T>(row + 32 * kb + 8 * g4);
   } else {
@@ -150,6 +162,21 @@ __device__ __forceinline__ Frag<T> gload_frag(const T* __restrict__ row, int kb,
     }
   }
   return f;
+}
+
+// Zero a fragment without branching (rows past the chunk end).
+template <typename T>
+__device__ __forceinline__ Frag<T> keep_if(const Frag<T>& f, bool keep) {
+  Frag<T> r;
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { r.lo[j] = keep ? f.lo[j] : 0.f; r.hi[j] = keep ? f.hi[j] : 0.f; }
+  } else {
+    const auto u = __builtin_bit_cast(uint4, f.v);
+    const uint4 z = keep ? u : make_uint4(0, 0, 0, 0);
+    r.v = __builtin_bit_cast(decltype(r.v), z);
+  }
+  return r;
 }
 
 template <typename T, int DK>
@@ -185,13 +212,9 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
   const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (item >= nitems) return;
   const int gc = item / p.Hv, h = item % p.Hv;
-  const int nchunks = p.chunk_offsets[p.B];
-  if (gc >= nchunks) return;
-  const int s = find_seq(p.chunk_offsets, p.B, gc);
-  int st0, st1;
-  seq_range(p.cu, p.T, p.total, s, st0, st1);
-  const int t0 = st0 + (gc - p.chunk_offsets[s]) * C;
-  const int len = min(C, st1 - t0);
+  const int2 info = reinterpret_cast<const int2*>(p.chunk_info)[gc];
+  const int t0 = info.x, len = info.y;
+  if (len <= 0) return;
   const int lane = threadIdx.x;
   const int i16 = lane & 15, g4 = lane >> 4;
   const int hk = h / (p.Hv / p.Hq);
@@ -200,23 +223,26 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
   // ---- K fragments of every row tile, Q fragments of row tile 0 -------------
   const T* kp = static_cast<const T*>(p.k);
   const T* qp = static_cast<const T*>(p.q);
-  const size_t lane_off = ((size_t)(t0 + i16) * p.Hq + hk) * DK;
-  const size_t tile_step = (size_t)16 * p.Hq * DK;
+  auto row_off = [&](int r) { return ((size_t)(t0 + min(r, len - 1)) * p.Hq + hk) * DK; };
   Frag<T> kf[nrt][NKB], qf[NKB];
 #pragma unroll
   for (int r = 0; r < nrt; ++r)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) kf[r][kb] = gload_frag<T, DK>(kp + lane_off + r * tile_step, kb, g4, 16 * r + i16 < len);
+    for (int kb = 0; kb < NKB; ++kb) kf[r][kb] = gload_frag<T, DK>(kp + row_off(16 * r + i16), kb, g4);
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) qf[kb] = gload_frag<T, DK>(qp + lane_off, kb, g4, i16 < len);
+  for (int kb = 0; kb < NKB; ++kb) qf[kb] = gload_frag<T, DK>(qp + row_off(i16), kb, g4);
 
   // ---- log2 cumulative decay, beta, gamma and tail -------------------------
   {
-    float gv = 0.f, bv = 0.f;
-    if (lane < len) {
-      gv = p.g[(size_t)(t0 + lane) * p.Hv + h];
-      bv = p.beta[(size_t)(t0 + lane) * p.Hv + h];
-    }
+    const size_t gi = (size_t)(t0 + min(lane, len - 1)) * p.Hv + h;
+    const float gv = lane < len ? p.g[gi] : 0.f;
+    const float bv = lane < len ? p.beta[gi] : 0.f;
+#pragma unroll
+    for (int r = 0; r < nrt; ++r)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kf[r][kb] = keep_if<T>(kf[r][kb], 16 * r + i16 < len);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qf[kb] = keep_if<T>(qf[kb], i16 < len);
     float x = gv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -236,8 +262,7 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
     Frag<T> qn[NKB];
     if (r + 1 < nrt) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        qn[kb] = gload_frag<T, DK>(qp + lane_off + (r + 1) * tile_step, kb, g4, 16 * (r + 1) + i16 < len);
+      for (int kb = 0; kb < NKB; ++kb) qn[kb] = gload_frag<T, DK>(qp + row_off(16 * (r + 1) + i16), kb, g4);
     }
     f32x4 kq[nrt];
 #pragma unroll
@@ -264,7 +289,7 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
     }
     if (r + 1 < nrt) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) qf[kb] = qn[kb];
+      for (int kb = 0; kb < NKB; ++kb) qf[kb] = keep_if<T>(qn[kb], 16 * (r + 1) + i16 < len);
     }
   }
 #pragma unroll
@@ -455,11 +480,22 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
   T* SX = reinterpret_cast<T*>(fixed + SM::KTB);
   T* DX = reinterpret_cast<T*>(fixed + SM::KTB + SM::SXB);
 
-  const int slice = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // XCD-aware order: workgroup w runs on XCD w % 8.  The workgroups reading the
+  // same keys and queries -- every column slice of every value head of one
+  // (sequence, key head) group -- are given ids that agree mod 8, so they share
+  // one L2; groups are still dispatched in sequence order.
+  const int G = p.Hv / p.Hq, nsl = (p.dv + 63) / 64, GS = nsl * G;
+  const int xcd = (int)(blockIdx.x & 7), rnd = (int)(blockIdx.x >> 3);
+  const int grp = (rnd / GS) * 8 + xcd, mem = rnd % GS;
+  if (grp >= p.Hq * p.B) return;
+  const int s = grp / p.Hq, slice = mem % nsl, h = (grp % p.Hq) * G + mem / nsl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const bool chain = wave < 4;
   const int wq = wave & 3;                                      // column group
+  // the chain waves carry the sequential dependence: let them win instruction
+  // arbitration against the output wave that shares their SIMD
+  if (chain) __builtin_amdgcn_s_setprio(2);
   const int ncols = min(64, p.dv - 64 * slice);
   const int col0 = 64 * slice + 16 * wq;
   const bool active = 16 * wq < ncols;    // slices narrower than 64 columns idle some groups
@@ -794,7 +830,10 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     attr2 = true;
   }
   prof_begin(K_STATE, st);
-  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C>), dim3(nslices, a.Hv, a.B), dim3(512), sm2, st, a);
+  const long long groups = (long long)a.Hq * a.B;
+  const long long sblocks = 8LL * nslices * (a.Hv / a.Hq) * ((groups + 7) / 8);
+  if (sblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C>), dim3((unsigned)sblocks), dim3(512), sm2, st, a);
   prof_end(K_STATE, st);
   return hipGetLastError();
 }

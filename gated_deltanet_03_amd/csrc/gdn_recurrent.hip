@@ -8,43 +8,96 @@
 // support for GatedDeltaNet", section "Changes"]: a clamped per-row prefix of
 // (decay, shared key, delta) factors whose replay is S = decay*S + outer(key, delta).
 //
-// Design (memory-bound; no matrix cores): one wave64 owns a [dk x DVS] column
-// slice of one (row, value head) state.  Columns of S never interact (only the
-// dk-reductions S^T k and S^T q couple rows), so slices are independent.
-// Lane layout: lane = rg * CG + cg; cg picks 4 adjacent columns (one 16-byte
-// float4), rg picks RPL = dk / RG adjacent rows.  A wave's load of one row
-// index covers RG rows x DVS*4 contiguous bytes, fully using every 64/128-byte
-// segment.  The dk-reductions are a per-lane partial sum over RPL rows plus a
-// butterfly over the RG row groups.  The state is read once and written once
-// per call; token inputs for step t+1 are fetched while step t computes.
+// Design (memory- and VALU-bound; no matrix cores): one wave64 owns a
+// [dk x 16] column slice of one (row, value head) state.  Columns of S never
+// interact (only the dk-reductions S^T k and S^T q couple rows), so slices are
+// independent.  Lane layout: lane = rg * 4 + cg; cg picks 4 adjacent columns
+// (one 16-byte float4), rg picks RPL = dk / 16 adjacent rows.  The
+// dk-reductions are a per-lane partial sum over RPL rows plus a butterfly over
+// the 16 row groups done entirely on the VALU: two DPP row rotations (lanes
+// +-4, +-8 inside a row of 16) and the permlane16 / permlane32 swaps.
+// Token inputs are prefetched NPF tokens ahead as raw 16-byte words.  The 8
+// column slices of one (row, head) state get workgroup ids that agree mod 8,
+// so they run on one XCD and the two 64-byte halves of every 128-byte state
+// line are fetched once into its L2.  The state is read once and written once
+// per call.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-template <typename T, int DK, int DVS>
-struct DecodeGeom {
-  static constexpr int CG = DVS / 4;   // column groups (float4) per wave
-  static constexpr int RG = 64 / CG;   // row groups per wave
-  static constexpr int RPL = DK / RG;  // rows per lane
-  static_assert(RPL >= 1 && RG * RPL == DK, "unsupported dk / slice width");
+constexpr int DVS = 16;   // columns per wave
+constexpr int NPF = 4;    // token prefetch depth
+
+// sum over the 16 lanes sharing lane % 4
+__device__ __forceinline__ float sum_rowgroups(float x) {
+  x += __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xf, 0xf, false);   // row_ror:8
+  x += __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xf, 0xf, false);   // row_ror:4
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);                   // + lane ^ 16
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);                // + lane ^ 32
+}
+
+// N consecutive elements of T kept as raw 32-bit words until use.
+template <typename T, int N>
+struct Raw {
+  static constexpr int BYTES = N * (int)sizeof(T);
+  static constexpr int W = BYTES >= 4 ? BYTES / 4 : 1;
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const T* __restrict__ p) {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < BYTES / 16; ++i) {
+        const uint4 u = reinterpret_cast<const uint4*>(p)[i];
+        w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+      }
+    } else if constexpr (BYTES == 8) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      w[0] = u.x; w[1] = u.y;
+    } else if constexpr (BYTES == 4) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      static_assert(BYTES == 2, "unsupported row width");
+      w[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+  }
+  __device__ __forceinline__ float get(int i) const {
+    if constexpr (sizeof(T) == 4) {
+      return __uint_as_float(w[i]);
+    } else {
+      const uint16_t bits = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+      return Elem<T>::to_f(__builtin_bit_cast(T, bits));
+    }
+  }
 };
 
 template <typename T, int RPL>
 struct TokenIn {
-  float k[RPL];
-  float q[RPL];
-  float v[4];
+  Raw<T, RPL> k, q;
+  Raw<T, 4> v;
   float g, beta;
 };
 
-template <typename T, int DK, int DVS>
+// Workgroup id -> (row, value head, column slice) with the slices of one
+// (row, head) on one XCD (ids congruent mod 8); false for padding workgroups.
+__device__ __forceinline__ bool slice_of(int Hv, int nsl, int B, int& b, int& h, int& slice) {
+  const int xcd = (int)(blockIdx.x & 7), rnd = (int)(blockIdx.x >> 3);
+  const int grp = (rnd / nsl) * 8 + xcd;
+  if (grp >= B * Hv) return false;
+  slice = rnd % nsl;
+  b = grp / Hv;
+  h = grp % Hv;
+  return true;
+}
+
+template <typename T, int DK>
 __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
-  using Gm = DecodeGeom<T, DK, DVS>;
-  constexpr int CG = Gm::CG, RPL = Gm::RPL;
+  constexpr int RPL = DK / 16;
   const int lane = threadIdx.x;
-  const int cg = lane % CG, rg = lane / CG;
-  const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int cg = lane & 3, rg = lane >> 2;
+  int b, h, slice;
+  if (!slice_of(p.Hv, p.dv / DVS, p.B, b, h, slice)) return;
   const int G = p.Hv / p.Hq;
   const int hk = h / G;
   const int dv = p.dv;
@@ -61,15 +114,17 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
 
   auto load_tok = [&](int t, TokenIn<T, RPL>& in) {
     const size_t qk = ((size_t)t * p.Hq + hk) * DK + row0;
-    load_row_f32<T, RPL>(kp + qk, in.k);
-    load_row_f32<T, RPL>(qp + qk, in.q);
-    load_row_f32<T, 4>(vp + ((size_t)t * p.Hv + h) * dv + col, in.v);
+    in.k.load(kp + qk);
+    in.q.load(qp + qk);
+    in.v.load(vp + ((size_t)t * p.Hv + h) * dv + col);
     in.g = p.g[(size_t)t * p.Hv + h];
     in.beta = p.beta[(size_t)t * p.Hv + h];
   };
 
-  TokenIn<T, RPL> nxt;
-  if (t0 < t1) load_tok(t0, nxt);
+  TokenIn<T, RPL> ring[NPF];
+#pragma unroll
+  for (int u = 0; u < NPF; ++u)
+    if (t0 + u < t1) load_tok(t0 + u, ring[u]);
 
   // State slice: rows row0..row0+RPL-1, columns col..col+3.
   float4 S[RPL];
@@ -92,61 +147,63 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
   const size_t R = (size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * dv;
   const bool write_key = (h % G == 0) && slice == 0 && cg == 0;
 
-  for (int t = t0; t < t1; ++t) {
-    TokenIn<T, RPL> in = nxt;
-    if (t + 1 < t1) load_tok(t + 1, nxt);
-    const float a = expf(in.g);
+  for (int tb = t0; tb < t1; tb += NPF) {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int t = tb + u;
+      if (t >= t1) break;
+      const TokenIn<T, RPL> in = ring[u];
+      if (t + NPF < t1) load_tok(t + NPF, ring[u]);
+      const float a = expf(in.g);
+      float kr[RPL];
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) kr[r] = in.k.get(r);
 
-    // Partial dk-reductions over this lane's rows: u = S^T k, w = S^T q, kq = k.q
-    float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
-    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, kq = 0.f;
+      // Partial dk-reductions over this lane's rows: u = S^T k, w = S^T q, kq = k.q
+      float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
+      float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, kq = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const float kr = in.k[r], qr = in.q[r];
-      u0 = fmaf(S[r].x, kr, u0); u1 = fmaf(S[r].y, kr, u1);
-      u2 = fmaf(S[r].z, kr, u2); u3 = fmaf(S[r].w, kr, u3);
-      w0 = fmaf(S[r].x, qr, w0); w1 = fmaf(S[r].y, qr, w1);
-      w2 = fmaf(S[r].z, qr, w2); w3 = fmaf(S[r].w, qr, w3);
-      kq = fmaf(kr, qr, kq);
-    }
+      for (int r = 0; r < RPL; ++r) {
+        const float qr = in.q.get(r);
+        u0 = fmaf(S[r].x, kr[r], u0); u1 = fmaf(S[r].y, kr[r], u1);
+        u2 = fmaf(S[r].z, kr[r], u2); u3 = fmaf(S[r].w, kr[r], u3);
+        w0 = fmaf(S[r].x, qr, w0); w1 = fmaf(S[r].y, qr, w1);
+        w2 = fmaf(S[r].z, qr, w2); w3 = fmaf(S[r].w, qr, w3);
+        kq = fmaf(kr[r], qr, kq);
+      }
+      u0 = sum_rowgroups(u0); u1 = sum_rowgroups(u1); u2 = sum_rowgroups(u2); u3 = sum_rowgroups(u3);
+      w0 = sum_rowgroups(w0); w1 = sum_rowgroups(w1); w2 = sum_rowgroups(w2); w3 = sum_rowgroups(w3);
+      kq = sum_rowgroups(kq);
+      // delta = beta (v - alpha S^T k); o = scale (alpha S^T q + delta (k.q)) = scale S_t^T q
+      const float d0 = in.beta * (in.v.get(0) - a * u0);
+      const float d1 = in.beta * (in.v.get(1) - a * u1);
+      const float d2 = in.beta * (in.v.get(2) - a * u2);
+      const float d3 = in.beta * (in.v.get(3) - a * u3);
 #pragma unroll
-    for (int m = CG; m < 64; m <<= 1) {
-      u0 += __shfl_xor(u0, m); u1 += __shfl_xor(u1, m);
-      u2 += __shfl_xor(u2, m); u3 += __shfl_xor(u3, m);
-      w0 += __shfl_xor(w0, m); w1 += __shfl_xor(w1, m);
-      w2 += __shfl_xor(w2, m); w3 += __shfl_xor(w3, m);
-      kq += __shfl_xor(kq, m);
-    }
-    // delta = beta (v - alpha S^T k); o = scale (alpha S^T q + delta (k.q)) = scale S_t^T q
-    const float d0 = in.beta * (in.v[0] - a * u0);
-    const float d1 = in.beta * (in.v[1] - a * u1);
-    const float d2 = in.beta * (in.v[2] - a * u2);
-    const float d3 = in.beta * (in.v[3] - a * u3);
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const float kr = in.k[r];
-      S[r].x = fmaf(kr, d0, a * S[r].x);
-      S[r].y = fmaf(kr, d1, a * S[r].y);
-      S[r].z = fmaf(kr, d2, a * S[r].z);
-      S[r].w = fmaf(kr, d3, a * S[r].w);
-    }
-    if (rg == 0) {
-      store4<T>(op + ((size_t)t * p.Hv + h) * dv + col,
-                p.scale * fmaf(d0, kq, a * w0), p.scale * fmaf(d1, kq, a * w1),
-                p.scale * fmaf(d2, kq, a * w2), p.scale * fmaf(d3, kq, a * w3));
-    }
-    const int tt = t - t0;
-    if (tt < ncap) {
-      float* rec = p.su + ((size_t)b * p.cap + tt) * R;
-      if (slice == 0 && lane == 0) rec[h] = a;
-      if (write_key) {
-        float* kd = rec + p.Hv + (size_t)hk * DK + row0;
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) kd[r] = in.k[r];
+      for (int r = 0; r < RPL; ++r) {
+        S[r].x = fmaf(kr[r], d0, a * S[r].x);
+        S[r].y = fmaf(kr[r], d1, a * S[r].y);
+        S[r].z = fmaf(kr[r], d2, a * S[r].z);
+        S[r].w = fmaf(kr[r], d3, a * S[r].w);
       }
       if (rg == 0) {
-        float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;
-        dd[0] = d0; dd[1] = d1; dd[2] = d2; dd[3] = d3;
+        store4<T>(op + ((size_t)t * p.Hv + h) * dv + col,
+                  p.scale * fmaf(d0, kq, a * w0), p.scale * fmaf(d1, kq, a * w1),
+                  p.scale * fmaf(d2, kq, a * w2), p.scale * fmaf(d3, kq, a * w3));
+      }
+      const int tt = t - t0;
+      if (tt < ncap) {
+        float* rec = p.su + ((size_t)b * p.cap + tt) * R;
+        if (slice == 0 && lane == 0) rec[h] = a;
+        if (write_key) {
+          float* kd = rec + p.Hv + (size_t)hk * DK + row0;
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) kd[r] = kr[r];
+        }
+        if (rg == 0) {   // records are only 4-byte aligned in general (R need not be a multiple of 4)
+          float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;
+          dd[0] = d0; dd[1] = d1; dd[2] = d2; dd[3] = d3;
+        }
       }
     }
   }
@@ -159,13 +216,18 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
   }
 }
 
-template <int DK, int DVS>
+// Replay of captured records.  Records are fetched RB at a time (all their
+// loads issued before the first is applied) since each application is only two
+// VALU operations per state element.
+constexpr int RB = 8;
+
+template <int DK>
 __global__ __launch_bounds__(64) void replay_kernel(ReplayArgs p) {
-  using Gm = DecodeGeom<float, DK, DVS>;
-  constexpr int CG = Gm::CG, RPL = Gm::RPL;
+  constexpr int RPL = DK / 16;
   const int lane = threadIdx.x;
-  const int cg = lane % CG, rg = lane / CG;
-  const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int cg = lane & 3, rg = lane >> 2;
+  int b, h, slice;
+  if (!slice_of(p.Hv, p.dv / DVS, p.B, b, h, slice)) return;
   const int hk = h / (p.Hv / p.Hq);
   const int dv = p.dv;
   const int col = slice * DVS + cg * 4;
@@ -181,20 +243,33 @@ __global__ __launch_bounds__(64) void replay_kernel(ReplayArgs p) {
   for (int r = 0; r < RPL; ++r) S[r] = *reinterpret_cast<const float4*>(st + (size_t)(row0 + r) * dv + col);
 
   const size_t R = (size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * dv;
-  for (int c = 0; c < m; ++c) {
-    const float* rec = p.su + ((size_t)b * p.cap + c) * R;
-    const float a = rec[h];
-    const float* kr = rec + p.Hv + (size_t)hk * DK + row0;
-    const float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;
-    const float d0 = dd[0], d1 = dd[1], d2 = dd[2], d3 = dd[3];
+  const float* base = p.su + (size_t)b * p.cap * R;
+  for (int c0 = 0; c0 < m; c0 += RB) {
+    float a[RB];
+    float kk[RB][RPL];
+    float4 d[RB];
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const float k = kr[r];
-      // same operation order as the recurrent step: fma(k, delta, alpha * S)
-      S[r].x = fmaf(k, d0, a * S[r].x);
-      S[r].y = fmaf(k, d1, a * S[r].y);
-      S[r].z = fmaf(k, d2, a * S[r].z);
-      S[r].w = fmaf(k, d3, a * S[r].w);
+    for (int j = 0; j < RB; ++j) {
+      const int c = min(c0 + j, m - 1);   // in-range record; unused copies are discarded
+      const float* rec = base + (size_t)c * R;
+      a[j] = rec[h];
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) kk[j][r] = rec[p.Hv + (size_t)hk * DK + row0 + r];
+      const float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;   // 4-byte aligned only
+      d[j] = make_float4(dd[0], dd[1], dd[2], dd[3]);
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      if (c0 + j >= m) break;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const float k = kk[j][r];
+        // same operation order as the recurrent step: fma(k, delta, alpha * S)
+        S[r].x = fmaf(k, d[j].x, a[j] * S[r].x);
+        S[r].y = fmaf(k, d[j].y, a[j] * S[r].y);
+        S[r].z = fmaf(k, d[j].z, a[j] * S[r].z);
+        S[r].w = fmaf(k, d[j].w, a[j] * S[r].w);
+      }
     }
   }
 #pragma unroll
@@ -222,17 +297,17 @@ __global__ __launch_bounds__(256) void copy_kernel(const float* __restrict__ src
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+// Padded 1-D grid for the XCD-aware slice order: 8 * nsl * ceil(B*Hv / 8).
+static unsigned slice_grid(int B, int Hv, int dv) {
+  const long long groups = (long long)B * Hv;
+  return (unsigned)(8LL * (dv / DVS) * ((groups + 7) / 8));
+}
+
 template <typename T, int DK>
 static hipError_t launch_rec_dk(const DecodeArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   prof_begin(K_RECURRENT, s);
-  if (a.dv >= 32) {
-    dim3 grid(a.dv / 32, a.Hv, a.B);
-    hipLaunchKernelGGL((recurrent_step_kernel<T, DK, 32>), grid, dim3(64), 0, s, a);
-  } else {
-    dim3 grid(a.dv / 16, a.Hv, a.B);
-    hipLaunchKernelGGL((recurrent_step_kernel<T, DK, 16>), grid, dim3(64), 0, s, a);
-  }
+  hipLaunchKernelGGL((recurrent_step_kernel<T, DK>), dim3(slice_grid(a.B, a.Hv, a.dv)), dim3(64), 0, s, a);
   prof_end(K_RECURRENT, s);
   return hipGetLastError();
 }
@@ -261,11 +336,7 @@ template <int DK>
 static hipError_t launch_replay_dk(const ReplayArgs& a, hipStream_t s) {
   if (a.B == 0 || a.cap == 0) return hipSuccess;
   prof_begin(K_REPLAY, s);
-  if (a.dv >= 32) {
-    hipLaunchKernelGGL((replay_kernel<DK, 32>), dim3(a.dv / 32, a.Hv, a.B), dim3(64), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((replay_kernel<DK, 16>), dim3(a.dv / 16, a.Hv, a.B), dim3(64), 0, s, a);
-  }
+  hipLaunchKernelGGL((replay_kernel<DK>), dim3(slice_grid(a.B, a.Hv, a.dv)), dim3(64), 0, s, a);
   prof_end(K_REPLAY, s);
   return hipGetLastError();
 }

@@ -107,7 +107,9 @@ def test_workspace_validation_and_sizing(lib):
     assert gdn.gdn_prefill_workspace_bytes(sh, 48, False) == 0
     assert gdn.gdn_prefill_workspace_bytes(shape(dk=96), 64, False) == 0
     rag = gdn.gdn_prefill_workspace_bytes(shape(B=4, T=14286, Hq=16, Hv=32), 64, True)
-    assert rag == 256 + (14286 // 64 + 4 + 1) * 32 * (2 * 6 * 512 * 2 + 512)
+    max_chunks = 14286 // 64 + 4 + 1
+    head = -(-(32 + max_chunks * 8) // 256) * 256      # offsets (B+1, padded to 16 B) + chunk table
+    assert rag == head + max_chunks * 32 * (2 * 6 * 512 * 2 + 512)
     assert prefill(lib, sh, ws=NULL, wsb=0) == gdn.GDN_ERR_INVALID_ARG and "workspace" in last(lib)
     assert prefill(lib, sh, ws=ctypes.c_void_p(0x40000008), wsb=need) == gdn.GDN_ERR_INVALID_ARG
 
