@@ -29,7 +29,7 @@ with decay = alpha_t, key = k_t, delta = delta_t):
     o_t     = scale * S_t^T q_t            (post-update state)
 
 S is [dk, dv] per (sequence, value head); value head h reads key/query head
-h // (Hv / Hq).  Readings of what the pages leave open are listed in DESIGN.md.
+h // (Hv / Hq) (contiguous groups of value heads share a key head).
 
 Parity status: pinned (tests/test_oracle_pins.py) except the head map above,
 which is a convention ("parity unpinned" beyond it).
