@@ -617,6 +617,30 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
     if (nch > 0) issue(0, 0);
   }
 
+  // B fragment selecting the 16 columns of this group out of a 32-slot V row
+  // fragment (slots 8g + j, g < 2, read columns 16 wq + 8g + j): V times it is
+  // V in accumulator layout, exactly (products with 1 and 0)
+  Frag<T> vsel;
+  {
+    f32x4 plo, phi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      plo[j] = (g4 < 2 && 8 * g4 + j == i16) ? 1.f : 0.f;
+      phi[j] = (g4 < 2 && 8 * g4 + 4 + j == i16) ? 1.f : 0.f;
+    }
+    vsel = make_frag<T>(plo, phi);
+  }
+  // V fragment of token row `tok`: columns 16 wq + 8 (g & 1) .. +7 of the slice
+  auto v_frag = [&](const unsigned char* Vs, int tok) {
+    const int pc = (16 * wq + 8 * (g4 & 1)) * ES / 16;   // first 16-byte piece
+    const T* a = reinterpret_cast<const T*>(Vs + tok * rowbv + (((pc) ^ (tok & (pprv - 1))) << 4));
+    if constexpr (ES == 2) {
+      return load_frag_native<T>(a);
+    } else {
+      const T* b = reinterpret_cast<const T*>(Vs + tok * rowbv + (((pc + 1) ^ (tok & (pprv - 1))) << 4));
+      return load_frag_rows<T>(a, b);
+    }
+  };
   const size_t ostride = (size_t)p.Hv * dv;
   const size_t olane = (size_t)(4 * g4) * ostride + (size_t)h * dv + col0 + i16;
 
@@ -637,37 +661,41 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
     Frag<T> Tb0, Tb1;
     if (chain) {
       if (SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
-      // ---- KS = K S ------------------------------------------------------------
+      // ---- every LDS read of this chunk that does not depend on the state,
+      //      issued together ahead of the products ---------------------------------
+      Frag<T> ak[NSB][nrt], av[nrt];
+#pragma unroll
+      for (int kb = 0; kb < NSB; ++kb)
+#pragma unroll
+        for (int r = 0; r < nrt; ++r) ak[kb][r] = kq_frag(Kt, 16 * r + i16, kb);
+#pragma unroll
+      for (int r = 0; r < nrt; ++r) av[r] = v_frag(Vs, 16 * r + i16);
+      f32x4 gm[4];
+#pragma unroll
+      for (int r = 0; r < nrt; ++r) gm[r] = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- KS = K S, V in accumulator layout ---------------------------------
       Frag<T> Sb[NSB];
 #pragma unroll
       for (int kb = 0; kb < NSB; ++kb)
         Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 KSa[4];
+      f32x4 KSa[4], Va[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) KSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) KSa[r] = Va[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NSB; ++kb) {
-        Frag<T> ak[nrt];
+      for (int r = 0; r < nrt; ++r) mma<T>(Va[r], av[r], vsel);
 #pragma unroll
-        for (int r = 0; r < nrt; ++r) ak[r] = kq_frag(Kt, 16 * r + i16, kb);
+      for (int kb = 0; kb < NSB; ++kb)
 #pragma unroll
-        for (int r = 0; r < nrt; ++r) mma<T>(KSa[r], ak[r], Sb[kb]);
-      }
+        for (int r = 0; r < nrt; ++r) mma<T>(KSa[r], ak[kb][r], Sb[kb]);
       // ---- X = V - gamma * KS ------------------------------------------------
       f32x4 X[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         X[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (r < nrt) {
-          const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
-          const int cb = (16 * wq + i16) * ES;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int tok = 16 * r + 4 * g4 + q;
-            const T* vv = reinterpret_cast<const T*>(Vs + tok * rowbv + ((((cb >> 4) ^ (tok & (pprv - 1)))) << 4) +
-                                                     (cb & 15));
-            X[r][q] = Elem<T>::to_f(*vv) - gm[q] * KSa[r][q];
-          }
+          for (int q = 0; q < 4; ++q) X[r][q] = Va[r][q] - gm[r][q] * KSa[r][q];
         }
       }
       const Frag<T> Xb0 = make_frag<T>(X[0], X[1]), Xb1 = make_frag<T>(X[2], X[3]);
@@ -695,15 +723,18 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
       // ---- QS = Q S (state fragments from the chain wave) ----------------------
 #pragma unroll
       for (int r = 0; r < 4; ++r) QSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Frag<T> sbf[NSB], aq[NSB][nrt];
 #pragma unroll
       for (int kb = 0; kb < NSB; ++kb) {
-        const Frag<T> sbf = load_frag_native<T>(sx_mine + kb * 512);
-        Frag<T> aq[nrt];
+        sbf[kb] = load_frag_native<T>(sx_mine + kb * 512);
 #pragma unroll
-        for (int r = 0; r < nrt; ++r) aq[r] = kq_frag(Qt, 16 * r + i16, kb);
-#pragma unroll
-        for (int r = 0; r < nrt; ++r) mma<T>(QSa[r], aq[r], sbf);
+        for (int r = 0; r < nrt; ++r) aq[kb][r] = kq_frag(Qt, 16 * r + i16, kb);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < NSB; ++kb)
+#pragma unroll
+        for (int r = 0; r < nrt; ++r) mma<T>(QSa[r], aq[kb][r], sbf[kb]);
       // ---- K^T fragments: fragment (state tile rt, token block kb) holds, for
       //      state row 16rt + n, K[32kb + 4g + j][dk(16rt + n)] (lo) and the same
       //      16 tokens later (hi): tiles D(2kb, rt), D(2kb+1, rt) of K * P, P the
@@ -739,19 +770,25 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
     }
     lds_barrier();   // MID: Delta and K^T fragments are in LDS; state fragments consumed
     if (chain) {
-      if (SM::NBUF == 1 && c + 1 < nch) issue(c + 1, 0);
       // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
       const float gl = GT[C - 1];
 #pragma unroll
       for (int r = 0; r < NST; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) S[r][q] *= gl;
+      Frag<T> kt[2][NST];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (2 * kb < nrt) {
+#pragma unroll
+          for (int r = 0; r < NST; ++r) kt[kb][r] = load_frag_native<T>(KT + ((2 * r + kb) * 64 + lane) * 8);
+        }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb < nrt) {
 #pragma unroll
-          for (int r = 0; r < NST; ++r)
-            mma<T>(S[r], load_frag_native<T>(KT + ((2 * r + kb) * 64 + lane) * 8), kb == 0 ? Tb0 : Tb1);
+          for (int r = 0; r < NST; ++r) mma<T>(S[r], kt[kb][r], kb == 0 ? Tb0 : Tb1);
         }
       }
       // next chunk's state fragments for the output wave
@@ -788,6 +825,12 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
               if (16 * r + 4 * g4 + q < len) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
         }
       }
+    }
+    if constexpr (SM::NBUF == 1) {
+      // single stage buffer: chunk c+1 may only overwrite it once every wave is
+      // done reading chunk c (gamma, tail and MP are read after MID)
+      lds_barrier();
+      if (chain && c + 1 < nch) issue(c + 1, 0);
     }
   }
 
