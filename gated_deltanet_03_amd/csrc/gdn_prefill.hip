@@ -4,7 +4,7 @@
 //                         ceil(len_s / C)) into the workspace header.
 //  2. chunk_prep_kernel   fully parallel over (chunk, key head): everything that
 //                         does not depend on the carried state.
-//  3. chunk_state_kernel  parallel over (sequence, value head, 64-column slice),
+//  3. chunk_state_kernel  parallel over (sequence, value head, column slice),
 //                         sequential over the chunks of the sequence: the state
 //                         contractions, with S kept in fp32 accumulators.
 //
@@ -398,12 +398,13 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. state pass: grid (slices of 64 columns, Hv, B), 512 threads = 8 waves.
+// 3. state pass: one workgroup per (sequence, value head, slice of 16*NG columns),
+//    2*NG waves (NG = 2 or 4 column groups of 16).
 //
 //    Each 16-column group of the slice is served by two waves that share a
-//    SIMD: a chain wave (waves 0-3) owning the fp32 state of those columns and
+//    SIMD: a chain wave (waves 0..NG-1) owning the fp32 state of those columns and
 //    running the sequential part, K*S -> X -> A'*X -> S update; and an output
-//    wave (waves 4-7) running everything off that path: Q*S, the K^T fragments,
+//    wave (waves NG..2NG-1) running everything off that path: Q*S, the K^T fragments,
 //    MP*Delta and the o stores.  The state crosses over as bf16/f16 fragments
 //    (written by the chain wave after each update), Delta goes the other way.
 //
@@ -443,9 +444,10 @@ __device__ __forceinline__ int perm_dk(int r) {
   }
 }
 
-template <typename T, int DK>
+template <typename T, int DK, int NG>
 struct StateSmem {
   static constexpr int ES = (int)sizeof(T);
+  static constexpr int SW = 16 * NG;                // columns per workgroup (NG groups of 16)
   static constexpr int PER = 16 / ES;               // elements per 16-byte piece
   static constexpr int PPR = DK / PER;              // pieces per K/Q row
   static constexpr int ROWB = DK * ES;              // bytes per K/Q row
@@ -454,12 +456,12 @@ struct StateSmem {
   static constexpr int NKT = 2 * NST;               // K^T fragments (dk tile, token block)
   static constexpr int FB = FRAG * ES;              // bytes per fragment block
   static constexpr int KB = 64 * ROWB;              // K (or Q) tile bytes
-  static constexpr int VB = 64 * 64 * ES;           // V tile bytes (up to 64 columns)
+  static constexpr int VB = 64 * SW * ES;           // V tile bytes (up to SW columns)
   static constexpr int AB = 2 * NTRI * FB;          // A' and MP fragments
   static constexpr int STAGE = 2 * KB + VB + AB + 512;
   static constexpr int KTB = NKT * FB;              // K^T fragments
-  static constexpr int SXB = 4 * NSB * FB;          // state fragments, 4 column groups
-  static constexpr int DXB = 4 * 2 * FB;            // Delta fragments, 4 column groups
+  static constexpr int SXB = NG * NSB * FB;         // state fragments, one set per column group
+  static constexpr int DXB = NG * 2 * FB;           // Delta fragments, one set per column group
   static constexpr int FIXED = KTB + SXB + DXB;
   static constexpr int NBUF = 2 * STAGE + FIXED <= 160 * 1024 ? 2 : 1;
   static constexpr size_t total = (size_t)NBUF * STAGE + FIXED;
@@ -467,9 +469,10 @@ struct StateSmem {
   static constexpr int OK_ = 0, OQ = KB, OV = 2 * KB, OA = 2 * KB + VB, OG = 2 * KB + VB + AB;
 };
 
-template <typename T, int DK, int C>
-__global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
-  using SM = StateSmem<T, DK>;
+template <typename T, int DK, int C, int NG>
+__global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
+  using SM = StateSmem<T, DK, NG>;
+  constexpr int SW = SM::SW;
   constexpr int nrt = C / 16;
   constexpr int NST = SM::NST, NSB = SM::NSB, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
   constexpr int RPI_K = 64 / PPR;         // K rows per DMA instruction
@@ -484,21 +487,21 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
   // same keys and queries -- every column slice of every value head of one
   // (sequence, key head) group -- are given ids that agree mod 8, so they share
   // one L2; groups are still dispatched in sequence order.
-  const int G = p.Hv / p.Hq, nsl = (p.dv + 63) / 64, GS = nsl * G;
+  const int G = p.Hv / p.Hq, nsl = (p.dv + SW - 1) / SW, GS = nsl * G;
   const int xcd = (int)(blockIdx.x & 7), rnd = (int)(blockIdx.x >> 3);
   const int grp = (rnd / GS) * 8 + xcd, mem = rnd % GS;
   if (grp >= p.Hq * p.B) return;
   const int s = grp / p.Hq, slice = mem % nsl, h = (grp % p.Hq) * G + mem / nsl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const bool chain = wave < 4;
-  const int wq = wave & 3;                                      // column group
+  const bool chain = wave < NG;
+  const int wq = wave & (NG - 1);                               // column group
   // the chain waves carry the sequential dependence: let them win instruction
   // arbitration against the output wave that shares their SIMD
   if (chain) __builtin_amdgcn_s_setprio(2);
-  const int ncols = min(64, p.dv - 64 * slice);
-  const int col0 = 64 * slice + 16 * wq;
-  const bool active = 16 * wq < ncols;    // slices narrower than 64 columns idle some groups
+  const int ncols = min(SW, p.dv - SW * slice);
+  const int col0 = SW * slice + 16 * wq;
+  const bool active = 16 * wq < ncols;    // slices narrower than SW columns idle some groups
   const int i16 = lane & 15, g4 = lane >> 4;
   const int hk = h / (p.Hv / p.Hq);
   const int dv = p.dv;
@@ -516,59 +519,77 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
   const T* vp = static_cast<const T*>(p.v);
   T* op = static_cast<T*>(p.o);
 
-  // ---- DMA slots of chain wave wq (compile-time counts, loop-invariant offsets)
-  constexpr int KPW = (PPR + 3) / 4, VPW = (64 / PER + 3) / 4, APW = (NA + 3) / 4;
-  int krow[KPW], koff[KPW], vrow[VPW], voff[VPW];
+  // ---- DMA slots of chain wave wq (compile-time counts, loop-invariant 32-bit
+  //      byte offsets from the chunk's wave-uniform base pointers, so each DMA
+  //      is one scalar-base + vector-offset load) -------------------------------
+  constexpr int KPW = (PPR + NG - 1) / NG, VPW = (SW / PER + NG - 1) / NG, APW = (NA + NG - 1) / NG;
+  int krow[KPW], vrow[VPW];
+  uint32_t kvo[KPW], vvo[VPW];
 #pragma unroll
   for (int m = 0; m < KPW; ++m) {
-    const int j = wq + 4 * m;
+    const int j = wq + NG * m;
     const int r = RPI_K * j + lane / PPR;
     const int pp = (lane % PPR) ^ (r % PPR);           // logical piece stored at this slot
     krow[m] = r;
-    koff[m] = (r * p.Hq + hk) * DK + pp * PER;
+    kvo[m] = (uint32_t)(((r * p.Hq + hk) * DK + pp * PER) * ES);
   }
 #pragma unroll
   for (int m = 0; m < VPW; ++m) {
-    const int j = wq + 4 * m;
+    const int j = wq + NG * m;
     const int r = rpiv * j + lane / pprv;
     const int pp = (lane % pprv) ^ (r % pprv);
     vrow[m] = r;
-    voff[m] = (r * p.Hv + h) * dv + 64 * slice + pp * PER;
+    vvo[m] = (uint32_t)(((r * p.Hv + h) * dv + SW * slice + pp * PER) * ES);
   }
   const int kq_row_stride = p.Hq * DK, v_row_stride = p.Hv * dv;
   auto issue = [&](int c, int buf) {
     const int t0 = st0 + c * C;
     const int last = min(C, st1 - t0) - 1;
-    const bool full = last == C - 1;                   // no row of this chunk needs clamping
     unsigned char* sb = smem_raw + buf * SM::STAGE;
-    const T* kc = kp + (size_t)t0 * kq_row_stride;
-    const T* qc = qp + (size_t)t0 * kq_row_stride;
-    const T* vc = vp + (size_t)t0 * v_row_stride;
+    const char* kc = reinterpret_cast<const char*>(kp + (size_t)t0 * kq_row_stride);
+    const char* qc = reinterpret_cast<const char*>(qp + (size_t)t0 * kq_row_stride);
+    const char* vc = reinterpret_cast<const char*>(vp + (size_t)t0 * v_row_stride);
     Block<T> blk(p.chunk_data, (size_t)(cbeg + c), p.Hv, h);
+    if (last == C - 1) {   // full chunk: no row needs clamping
 #pragma unroll
-    for (int m = 0; m < KPW; ++m) {
-      const int j = wq + 4 * m;
-      if (j < PPR) {
-        const int off = full ? koff[m] : koff[m] + (min(krow[m], last) - krow[m]) * kq_row_stride;
-        dma16(kc + off, sb + SM::OK_ + j * 1024);
-        dma16(qc + off, sb + SM::OQ + j * 1024);
+      for (int m = 0; m < KPW; ++m) {
+        const int j = wq + NG * m;
+        if (j < PPR) {
+          dma16(kc + kvo[m], sb + SM::OK_ + j * 1024);
+          dma16(qc + kvo[m], sb + SM::OQ + j * 1024);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < VPW; ++m) {
+        const int j = wq + NG * m;
+        if (j < pprv) dma16(vc + vvo[m], sb + SM::OV + j * 1024);
+      }
+    } else {               // last chunk of a sequence: rows past its end repeat its last row
+#pragma unroll
+      for (int m = 0; m < KPW; ++m) {
+        const int j = wq + NG * m;
+        if (j < PPR) {
+          const int64_t d = (int64_t)(min(krow[m], last) - krow[m]) * kq_row_stride * ES;
+          dma16(kc + kvo[m] + d, sb + SM::OK_ + j * 1024);
+          dma16(qc + kvo[m] + d, sb + SM::OQ + j * 1024);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < VPW; ++m) {
+        const int j = wq + NG * m;
+        if (j < pprv) dma16(vc + vvo[m] + (int64_t)(min(vrow[m], last) - vrow[m]) * v_row_stride * ES,
+                            sb + SM::OV + j * 1024);
       }
     }
-#pragma unroll
-    for (int m = 0; m < VPW; ++m) {
-      const int j = wq + 4 * m;
-      if (j < pprv) {
-        const int off = full ? voff[m] : voff[m] + (min(vrow[m], last) - vrow[m]) * v_row_stride;
-        dma16(vc + off, sb + SM::OV + j * 1024);
-      }
-    }
+    const char* ab = reinterpret_cast<const char*>(blk.A);
 #pragma unroll
     for (int m = 0; m < APW; ++m) {
-      const int j = wq + 4 * m;
-      if (j < NA) dma16(blk.A + (j * 64 + lane) * PER, sb + SM::OA + j * 1024);
+      const int j = wq + NG * m;
+      if (j < NA) dma16(ab + (uint32_t)((j * 64 + lane) * 16), sb + SM::OA + j * 1024);
     }
-    if (wq == 3 && lane < 32) dma16(blk.gam + 4 * lane, sb + SM::OG);
+    if (wq == NG - 1 && lane < 32) dma16(reinterpret_cast<const char*>(blk.gam) + 16 * lane, sb + SM::OG);
   };
+
 
   // fragment (row r, 32-wide dk block kb) of a swizzled K/Q tile: for dk >= 32
   // the 8 slots of group g are dk 32kb + 8g .. +7 (see perm_dk)
@@ -740,7 +761,7 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
       //      16 tokens later (hi): tiles D(2kb, rt), D(2kb+1, rt) of K * P, P the
       //      0/1 matrix picking dk column perm_dk(16rt + n) -------------------------
 #pragma unroll
-      for (int f0 = 0; f0 < SM::NKT; f0 += 4) {
+      for (int f0 = 0; f0 < SM::NKT; f0 += NG) {
         const int f = f0 + wq;
         if (f < SM::NKT) {
           const int rt = f >> 1, kb = f & 1;
@@ -846,6 +867,40 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(PrefillArgs p) {
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <typename T, int DK, int C, int NG>
+static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
+  using SM = StateSmem<T, DK, NG>;
+  const size_t sm2 = SM::total;
+  if (sm2 > 160 * 1024) return hipErrorInvalidValue;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C, NG>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int nslices = (a.dv + SM::SW - 1) / SM::SW;
+  const long long groups = (long long)a.Hq * a.B;
+  const long long sblocks = 8LL * nslices * (a.Hv / a.Hq) * ((groups + 7) / 8);
+  if (sblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  prof_begin(K_STATE, st);
+  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C, NG>), dim3((unsigned)sblocks), dim3(128 * NG), sm2, st, a);
+  prof_end(K_STATE, st);
+  return hipGetLastError();
+}
+
 template <typename T, int DK, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   prof_begin(K_PLAN, st);
@@ -862,22 +917,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     prof_end(K_PREP, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int nslices = (a.dv + 63) / 64;
-  const size_t sm2 = StateSmem<T, DK>::total;
-  if (sm2 > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr2 = false;
-  if (!attr2) {
-    e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sm2);
-    if (e != hipSuccess) return e;
-    attr2 = true;
-  }
-  prof_begin(K_STATE, st);
-  const long long groups = (long long)a.Hq * a.B;
-  const long long sblocks = 8LL * nslices * (a.Hv / a.Hq) * ((groups + 7) / 8);
-  if (sblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C>), dim3((unsigned)sblocks), dim3(512), sm2, st, a);
-  prof_end(K_STATE, st);
+  // Column groups per workgroup: 2 (32 columns, 4 waves) spreads each head over
+  // more CUs and halves the LDS and load traffic per CU per chunk, which
+  // shortens the sequential chunk step; 4 (64 columns, 8 waves) is kept for
+  // batches with more (sequence, head, slice) work than two workgroups per CU.
+  if ((long long)a.B * a.Hv * ((a.dv + 31) / 32) <= 2LL * device_cus())
+    e = launch_state<T, DK, C, 2>(a, st);
+  else
+    e = launch_state<T, DK, C, 4>(a, st);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
