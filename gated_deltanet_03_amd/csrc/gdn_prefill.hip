@@ -469,8 +469,8 @@ struct StateSmem {
   static constexpr int OK_ = 0, OQ = KB, OV = 2 * KB, OA = 2 * KB + VB, OG = 2 * KB + VB + AB;
 };
 
-template <typename T, int DK, int C, int NG>
-__global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
+template <typename T, int DK, int C, int NG, int NDW>
+__global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(PrefillArgs p) {
   using SM = StateSmem<T, DK, NG>;
   constexpr int SW = SM::SW;
   constexpr int nrt = C / 16;
@@ -495,7 +495,12 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const bool chain = wave < NG;
-  const int wq = wave & (NG - 1);                               // column group
+  // NDW > 0: waves 2NG.. only issue the chunk loads (they stall on the load
+  // address unit, which would otherwise stall the chain); NDW = 0: the chain
+  // waves issue them
+  const bool dmaw = NDW > 0 && wave >= 2 * NG;
+  const bool issuer = NDW > 0 ? dmaw : chain;
+  const int wq = wave & (NG - 1);                               // column group (load slot for loaders)
   // the chain waves carry the sequential dependence: let them win instruction
   // arbitration against the output wave that shares their SIMD
   if (chain) __builtin_amdgcn_s_setprio(2);
@@ -635,8 +640,8 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
     for (int kb = 0; kb < NSB; ++kb)
       store_frag_native<T>(sx_mine + kb * 512,
                            make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f}));
-    if (nch > 0) issue(0, 0);
   }
+  if (issuer && nch > 0) issue(0, 0);
 
   // B fragment selecting the 16 columns of this group out of a 32-slot V row
   // fragment (slots 8g + j, g < 2, read columns 16 wq + 8g + j): V times it is
@@ -669,9 +674,11 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
     const int buf = SM::NBUF == 2 ? (c & 1) : 0;
     const int t0 = st0 + c * C;
     const int len = min(C, st1 - t0);
-    // chunk c has landed (chain waves issued every DMA); chunk c-1 buffers are free
-    if (chain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // chunk c has landed (the issuing waves wait for their own loads); chunk c-1
+    // buffers are free
+    if (issuer) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
+    if (dmaw && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
     const unsigned char* sb = smem_raw + buf * SM::STAGE;
     const unsigned char* Kt = sb + SM::OK_;
     const unsigned char* Qt = sb + SM::OQ;
@@ -681,9 +688,9 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
     f32x4 QSa[4];
     Frag<T> Tb0, Tb1;
     if (chain) {
-      if (SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
       // ---- every LDS read of this chunk that does not depend on the state,
-      //      issued together ahead of the products ---------------------------------
+      //      issued together ahead of the products; the next chunk's loads are
+      //      issued behind them so their issue stalls overlap the LDS latency ---
       Frag<T> ak[NSB][nrt], av[nrt];
 #pragma unroll
       for (int kb = 0; kb < NSB; ++kb)
@@ -694,6 +701,8 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
       f32x4 gm[4];
 #pragma unroll
       for (int r = 0; r < nrt; ++r) gm[r] = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+      __builtin_amdgcn_sched_barrier(0);
+      if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
       // ---- KS = K S, V in accumulator layout ---------------------------------
       Frag<T> Sb[NSB];
@@ -740,7 +749,7 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
       }
       Tb0 = make_frag<T>(D[0], D[1]);
       Tb1 = make_frag<T>(D[2], D[3]);
-    } else {
+    } else if (!dmaw) {
       // ---- QS = Q S (state fragments from the chain wave) ----------------------
 #pragma unroll
       for (int r = 0; r < 4; ++r) QSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -817,7 +826,7 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
       for (int kb = 0; kb < NSB; ++kb)
         store_frag_native<T>(sx_mine + kb * 512,
                              make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f}));
-    } else {
+    } else if (!dmaw) {
       // ---- O = scale (gamma QS + MP Delta) -> o -----------------------------------
       const Frag<T> Db0 = load_frag_native<T>(dx_mine), Db1 = load_frag_native<T>(dx_mine + 512);
       f32x4 O[4];
@@ -851,7 +860,7 @@ __global__ __launch_bounds__(128 * NG) void chunk_state_kernel(PrefillArgs p) {
       // single stage buffer: chunk c+1 may only overwrite it once every wave is
       // done reading chunk c (gamma, tail and MP are read after MID)
       lds_barrier();
-      if (chain && c + 1 < nch) issue(c + 1, 0);
+      if (issuer && c + 1 < nch) issue(c + 1, 0);
     }
   }
 
@@ -879,14 +888,14 @@ static int device_cus() {
   return cached[dev];
 }
 
-template <typename T, int DK, int C, int NG>
+template <typename T, int DK, int C, int NG, int NDW>
 static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
   using SM = StateSmem<T, DK, NG>;
   const size_t sm2 = SM::total;
   if (sm2 > 160 * 1024) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C, NG>,
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C, NG, NDW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
     if (e != hipSuccess) return e;
     attr = true;
@@ -896,7 +905,8 @@ static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
   const long long sblocks = 8LL * nslices * (a.Hv / a.Hq) * ((groups + 7) / 8);
   if (sblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   prof_begin(K_STATE, st);
-  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C, NG>), dim3((unsigned)sblocks), dim3(128 * NG), sm2, st, a);
+  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C, NG, NDW>), dim3((unsigned)sblocks), dim3(64 * (2 * NG + NDW)),
+                     sm2, st, a);
   prof_end(K_STATE, st);
   return hipGetLastError();
 }
@@ -922,9 +932,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   // shortens the sequential chunk step; 4 (64 columns, 8 waves) is kept for
   // batches with more (sequence, head, slice) work than two workgroups per CU.
   if ((long long)a.B * a.Hv * ((a.dv + 31) / 32) <= 2LL * device_cus())
-    e = launch_state<T, DK, C, 2>(a, st);
+    e = launch_state<T, DK, C, 2, 2>(a, st);   // 6 waves: + two load-issuing waves
   else
-    e = launch_state<T, DK, C, 4>(a, st);
+    e = launch_state<T, DK, C, 4, 0>(a, st);   // 8 waves: the chain waves issue the loads
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
