@@ -27,6 +27,14 @@
 namespace gdn {
 
 constexpr int DVS = 16;   // columns per wave
+
+// State reads are ordinary loads: a replay right after a step reads the same
+// pre-step state and finds it in the caches.  State writes are not read again
+// by this call and are streamed out with non-temporal stores.
+__device__ __forceinline__ float4 load_state4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void store_state4(float* p, const float4& v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
 constexpr int NPF = 4;    // token prefetch depth
 
 // sum over the 16 lanes sharing lane % 4
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
     const float* s0 = p.s0 + (int64_t)b * p.s0_stride + (size_t)h * DK * dv;
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-      S[r] = *reinterpret_cast<const float4*>(s0 + (size_t)(row0 + r) * dv + col);
+      S[r] = load_state4(s0 + (size_t)(row0 + r) * dv + col);
   } else {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) S[r] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
     float* so = p.s_out + ((size_t)b * p.Hv + h) * DK * dv;
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-      *reinterpret_cast<float4*>(so + (size_t)(row0 + r) * dv + col) = S[r];
+      store_state4(so + (size_t)(row0 + r) * dv + col, S[r]);
   }
 }
 
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(64) void replay_kernel(ReplayArgs p) {
   float* st = p.state + ((size_t)b * p.Hv + h) * DK * dv;
   float4 S[RPL];
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) S[r] = *reinterpret_cast<const float4*>(st + (size_t)(row0 + r) * dv + col);
+  for (int r = 0; r < RPL; ++r) S[r] = load_state4(st + (size_t)(row0 + r) * dv + col);
 
   const size_t R = (size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * dv;
   const float* base = p.su + (size_t)b * p.cap * R;
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(64) void replay_kernel(ReplayArgs p) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) *reinterpret_cast<float4*>(st + (size_t)(row0 + r) * dv + col) = S[r];
+  for (int r = 0; r < RPL; ++r) store_state4(st + (size_t)(row0 + r) * dv + col, S[r]);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
