@@ -688,23 +688,24 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     f32x4 QSa[4];
     Frag<T> Tb0, Tb1;
     if (chain) {
-      // ---- every LDS read of this chunk that does not depend on the state,
-      //      issued together ahead of the products; the next chunk's loads are
-      //      issued behind them so their issue stalls overlap the LDS latency ---
-      Frag<T> ak[NSB][nrt], av[nrt];
-#pragma unroll
-      for (int kb = 0; kb < NSB; ++kb)
+      // ---- LDS reads and products in a fixed interleave: at most ~14 reads in
+      //      flight (the LDS counter a wait can name stops at 15), K blocks two
+      //      ahead of the products that use them, and gamma, A' and tail
+      //      prefetched behind the last K block ----------------------------------
+      constexpr int X1 = NSB >= 2 ? NSB - 2 : 0;   // step that prefetches gamma and A'
+      Frag<T> ak[NSB][nrt], av[nrt], aa[NTRI];
+      f32x4 gm[4], tl[4];
+      auto load_kblock = [&](int kb) {
 #pragma unroll
         for (int r = 0; r < nrt; ++r) ak[kb][r] = kq_frag(Kt, 16 * r + i16, kb);
+      };
+      load_kblock(0);
 #pragma unroll
       for (int r = 0; r < nrt; ++r) av[r] = v_frag(Vs, 16 * r + i16);
-      f32x4 gm[4];
-#pragma unroll
-      for (int r = 0; r < nrt; ++r) gm[r] = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+      if constexpr (NSB > 1) load_kblock(1);
       __builtin_amdgcn_sched_barrier(0);
       if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
-      // ---- KS = K S, V in accumulator layout ---------------------------------
       Frag<T> Sb[NSB];
 #pragma unroll
       for (int kb = 0; kb < NSB; ++kb)
@@ -713,11 +714,29 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
 #pragma unroll
       for (int r = 0; r < 4; ++r) KSa[r] = Va[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < nrt; ++r) mma<T>(Va[r], av[r], vsel);
-#pragma unroll
-      for (int kb = 0; kb < NSB; ++kb)
+      for (int kb = 0; kb < NSB; ++kb) {
 #pragma unroll
         for (int r = 0; r < nrt; ++r) mma<T>(KSa[r], ak[kb][r], Sb[kb]);
+        if (kb == 0) {
+#pragma unroll
+          for (int r = 0; r < nrt; ++r) mma<T>(Va[r], av[r], vsel);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb + 2 < NSB) load_kblock(kb + 2);
+        if (kb == X1) {
+#pragma unroll
+          for (int r = 0; r < nrt; ++r) gm[r] = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+#pragma unroll
+          for (int r = 0; r < nrt; ++r) aa[tri_idx(r, 0)] = load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8);
+#pragma unroll
+          for (int r = 2; r < nrt; ++r) aa[tri_idx(r, 1)] = load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8);
+        }
+        if (kb == NSB - 1) {
+#pragma unroll
+          for (int r = 0; r < nrt; ++r) tl[r] = *reinterpret_cast<const f32x4*>(GT + 64 + 16 * r + 4 * g4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // ---- X = V - gamma * KS ------------------------------------------------
       f32x4 X[4];
 #pragma unroll
@@ -734,19 +753,17 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         D[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (r < nrt) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8), Xb0);
+        if (r < nrt) mma<T>(D[r], aa[tri_idx(r, 0)], Xb0);
       }
 #pragma unroll
-      for (int r = 2; r < nrt; ++r) mma<T>(D[r], load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8), Xb1);
+      for (int r = 2; r < nrt; ++r) mma<T>(D[r], aa[tri_idx(r, 1)], Xb1);
       store_frag_native<T>(dx_mine, make_frag<T>(D[0], D[1]));
       store_frag_native<T>(dx_mine + 512, make_frag<T>(D[2], D[3]));
       // ---- tail-weighted Delta for the state update ---------------------------
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4 tl = *reinterpret_cast<const f32x4*>(GT + 64 + 16 * r + 4 * g4);
+      for (int r = 0; r < nrt; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) D[r][q] *= tl[q];
-      }
+        for (int q = 0; q < 4; ++q) D[r][q] *= tl[r][q];
       Tb0 = make_frag<T>(D[0], D[1]);
       Tb1 = make_frag<T>(D[2], D[3]);
     } else if (!dmaw) {
@@ -801,25 +818,24 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     lds_barrier();   // MID: Delta and K^T fragments are in LDS; state fragments consumed
     if (chain) {
       // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
+      // K^T fragments read eight ahead of the products that use them
+      constexpr int NKB2 = nrt > 2 ? 2 : 1, NU = NKB2 * NST, LA = 8;
+      Frag<T> kt[NU];
+#pragma unroll
+      for (int u = 0; u < NU && u < LA; ++u)
+        kt[u] = load_frag_native<T>(KT + ((2 * (u % NST) + u / NST) * 64 + lane) * 8);
       const float gl = GT[C - 1];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < NST; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) S[r][q] *= gl;
-      Frag<T> kt[2][NST];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (2 * kb < nrt) {
-#pragma unroll
-          for (int r = 0; r < NST; ++r) kt[kb][r] = load_frag_native<T>(KT + ((2 * r + kb) * 64 + lane) * 8);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (2 * kb < nrt) {
-#pragma unroll
-          for (int r = 0; r < NST; ++r) mma<T>(S[r], kt[kb][r], kb == 0 ? Tb0 : Tb1);
-        }
+      for (int u = 0; u < NU; ++u) {
+        mma<T>(S[u % NST], kt[u], u / NST == 0 ? Tb0 : Tb1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + LA < NU) kt[u + LA] = load_frag_native<T>(KT + ((2 * ((u + LA) % NST) + (u + LA) / NST) * 64 + lane) * 8);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // next chunk's state fragments for the output wave
 #pragma unroll
