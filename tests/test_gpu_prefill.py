@@ -138,9 +138,10 @@ def test_prefill_in_place_final_state(gdn):
 
 
 def test_prefix_snapshot_reuse(gdn):
-    """Prefill a 4096-token prefix, snapshot it, run batches of 16 x 256 branching
-    from the snapshot (stride-0 broadcast); the snapshot stays bit-identical and
-    sampled outputs match the oracle continuing from its own prefix state."""
+    """Prefill a 4096-token prefix, snapshot it, run 64 batches of 16 x 256
+    branching from the snapshot (stride-0 broadcast); the snapshot stays
+    bit-identical after every batch and sampled outputs of batches 0, 31 and 63
+    match the oracle continuing from its own prefix state."""
     pre = gi.make("prefix_reuse", part="prefix")
     say(f"case prefix_reuse prefix seed={pre['seed']}")
     _, pfin = prefill(gdn, pre, 64)
@@ -149,8 +150,8 @@ def test_prefix_snapshot_reuse(gdn):
     h0 = sha(snap)
     heads = [5, 26]
     pref = oracle_run(pre, heads=heads)
-    checked = {0, 3}
-    for bi in range(8):
+    checked = {0, 31, 63}
+    for bi in range(64):
         bt = gi.make("prefix_reuse", part="batch", batch_index=bi)
         o, fin = prefill(gdn, bt, 64, initial_state=snap, initial_state_batch_stride=0,
                          output_final_state=False)
