@@ -636,10 +636,16 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
 #pragma unroll
         for (int q = 0; q < 4; ++q) S[r][q] = s0[(size_t)perm_dk<DK>(16 * r + 4 * g4 + q) * dv];
     }
+  }
+  // 16-bit state fragments: B operand of the chain's K*S and, through LDS, of
+  // the output wave's Q*S; converted once per chunk after the state update
+  Frag<T> Sb[NSB];
+  if (chain) {
 #pragma unroll
-    for (int kb = 0; kb < NSB; ++kb)
-      store_frag_native<T>(sx_mine + kb * 512,
-                           make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f}));
+    for (int kb = 0; kb < NSB; ++kb) {
+      Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
+      store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
+    }
   }
   if (issuer && nch > 0) issue(0, 0);
 
@@ -706,10 +712,6 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       __builtin_amdgcn_sched_barrier(0);
       if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
-      Frag<T> Sb[NSB];
-#pragma unroll
-      for (int kb = 0; kb < NSB; ++kb)
-        Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 KSa[4], Va[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) KSa[r] = Va[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -837,11 +839,12 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         if (u + LA < NU) kt[u + LA] = load_frag_native<T>(KT + ((2 * ((u + LA) % NST) + (u + LA) / NST) * 64 + lane) * 8);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // next chunk's state fragments for the output wave
+      // next chunk's state fragments (kept for the chain's K*S, stored for the output wave)
 #pragma unroll
-      for (int kb = 0; kb < NSB; ++kb)
-        store_frag_native<T>(sx_mine + kb * 512,
-                             make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f}));
+      for (int kb = 0; kb < NSB; ++kb) {
+        Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
+        store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
+      }
     } else if (!dmaw) {
       // ---- O = scale (gamma QS + MP Delta) -> o -----------------------------------
       const Frag<T> Db0 = load_frag_native<T>(dx_mine), Db1 = load_frag_native<T>(dx_mine + 512);
