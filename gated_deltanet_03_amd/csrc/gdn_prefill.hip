@@ -196,7 +196,7 @@ __device__ __forceinline__ void mma_tn(f32x4& acc, const f32x4& e, const f32x4& 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T, int DK, int C>
-__global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int nrt = C / 16;
   constexpr int NKB = DK >= 32 ? DK / 32 : 1;
   constexpr float LOG2E = 1.4426950408889634f;
@@ -220,17 +220,18 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
   const int hk = h / (p.Hv / p.Hq);
   Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
 
-  // ---- K fragments of every row tile, Q fragments of row tile 0 -------------
+  // ---- K and Q fragments of every row tile (one batch of loads) ------------
   const T* kp = static_cast<const T*>(p.k);
   const T* qp = static_cast<const T*>(p.q);
   auto row_off = [&](int r) { return ((size_t)(t0 + min(r, len - 1)) * p.Hq + hk) * DK; };
-  Frag<T> kf[nrt][NKB], qf[NKB];
+  Frag<T> kf[nrt][NKB], qa[nrt][NKB];
 #pragma unroll
   for (int r = 0; r < nrt; ++r)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) kf[r][kb] = gload_frag<T, DK>(kp + row_off(16 * r + i16), kb, g4);
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) qf[kb] = gload_frag<T, DK>(qp + row_off(i16), kb, g4);
+    for (int kb = 0; kb < NKB; ++kb) {
+      kf[r][kb] = gload_frag<T, DK>(kp + row_off(16 * r + i16), kb, g4);
+      qa[r][kb] = gload_frag<T, DK>(qp + row_off(16 * r + i16), kb, g4);
+    }
 
   // ---- log2 cumulative decay, beta, gamma and tail -------------------------
   {
@@ -242,7 +243,9 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kf[r][kb] = keep_if<T>(kf[r][kb], 16 * r + i16 < len);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) qf[kb] = keep_if<T>(qf[kb], i16 < len);
+    for (int r = 0; r < nrt; ++r)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) qa[r][kb] = keep_if<T>(qa[r][kb], 16 * r + i16 < len);
     float x = gv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -259,17 +262,12 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
   // ---- MP = exp(G_i - G_j) (Q K^T)_ij, j <= i ------------------------------
 #pragma unroll
   for (int r = 0; r < nrt; ++r) {
-    Frag<T> qn[NKB];
-    if (r + 1 < nrt) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) qn[kb] = gload_frag<T, DK>(qp + row_off(16 * (r + 1) + i16), kb, g4);
-    }
     f32x4 kq[nrt];
 #pragma unroll
     for (int c = 0; c <= r; ++c) {
       kq[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kq[c], kf[c][kb], qf[kb]);
+      for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kq[c], kf[c][kb], qa[r][kb]);
     }
     const int i = 16 * r + i16;
     const float gi = Gs[i];
@@ -286,10 +284,6 @@ __global__ __launch_bounds__(64, 4) void chunk_prep_kernel(PrefillArgs p) {
     for (int kb = 0; kb <= r / 2; ++kb) {
       const f32x4 hi = 2 * kb + 1 <= r ? kq[2 * kb + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
       store_frag_native<T>(blk.MP + (tri_idx(r, kb) * 64 + lane) * 8, make_frag<T>(kq[2 * kb], hi));
-    }
-    if (r + 1 < nrt) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) qf[kb] = keep_if<T>(qn[kb], 16 * (r + 1) + i16 < len);
     }
   }
 #pragma unroll
