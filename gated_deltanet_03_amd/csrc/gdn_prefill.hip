@@ -195,30 +195,31 @@ __device__ __forceinline__ void mma_tn(f32x4& acc, const f32x4& e, const f32x4& 
 // which only drops terms already below fp32 resolution of the sums they enter).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T, int DK, int C>
+template <typename T, int DK, int C, int HPW>
 __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int nrt = C / 16;
   constexpr int NKB = DK >= 32 ? DK / 32 : 1;
   constexpr float LOG2E = 1.4426950408889634f;
-  __shared__ __align__(16) float Ld[4 * 16 * DS];   // diagonal blocks of L
-  __shared__ __align__(16) float Xd[4 * 16 * DS];   // their inverses, row-major
-  __shared__ __align__(16) float Gs[64];            // log2 cumulative decay
-  __shared__ __align__(16) float Bs[64];            // beta
+  __shared__ __align__(16) float Ld[HPW][4 * 16 * DS];   // diagonal blocks of L, per head
+  __shared__ __align__(16) float Xd[4 * 16 * DS];        // their inverses, row-major
+  __shared__ __align__(16) float Gs[HPW][64];            // log2 cumulative decay
+  __shared__ __align__(16) float Bs[HPW][64];            // beta
 
-  // XCD-aware order: workgroup w runs on XCD w % 8; give each XCD a contiguous
-  // run of (chunk, head) items so the value heads of one key head share an L2.
-  const int nitems = p.max_chunks * p.Hv;
+  // One item = (chunk, HPW value heads that share a key head).  XCD-aware
+  // order: workgroup w runs on XCD w % 8; each XCD gets a contiguous run of
+  // items so neighbouring key heads' rows share an L2.
+  const int npairs = p.Hv / HPW;
+  const int nitems = p.max_chunks * npairs;
   const int per = (nitems + 7) >> 3;
   const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (item >= nitems) return;
-  const int gc = item / p.Hv, h = item % p.Hv;
+  const int gc = item / npairs, h0 = (item % npairs) * HPW;
   const int2 info = reinterpret_cast<const int2*>(p.chunk_info)[gc];
   const int t0 = info.x, len = info.y;
   if (len <= 0) return;
   const int lane = threadIdx.x;
   const int i16 = lane & 15, g4 = lane >> 4;
-  const int hk = h / (p.Hv / p.Hq);
-  Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
+  const int hk = h0 / (p.Hv / p.Hq);
 
   // ---- K and Q fragments of every row tile (one batch of loads) ------------
   const T* kp = static_cast<const T*>(p.k);
@@ -233,19 +234,13 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
       qa[r][kb] = gload_frag<T, DK>(qp + row_off(16 * r + i16), kb, g4);
     }
 
-  // ---- log2 cumulative decay, beta, gamma and tail -------------------------
-  {
+  // ---- per head: log2 cumulative decay, beta, gamma and tail ---------------
+#pragma unroll
+  for (int v = 0; v < HPW; ++v) {
+    const int h = h0 + v;
     const size_t gi = (size_t)(t0 + min(lane, len - 1)) * p.Hv + h;
     const float gv = lane < len ? p.g[gi] : 0.f;
     const float bv = lane < len ? p.beta[gi] : 0.f;
-#pragma unroll
-    for (int r = 0; r < nrt; ++r)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kf[r][kb] = keep_if<T>(kf[r][kb], 16 * r + i16 < len);
-#pragma unroll
-    for (int r = 0; r < nrt; ++r)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) qa[r][kb] = keep_if<T>(qa[r][kb], 16 * r + i16 < len);
     float x = gv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -253,13 +248,22 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
       if (lane >= off) x += y;
     }
     const float glast = __shfl(x, C - 1);
-    Gs[lane] = x * LOG2E;
-    Bs[lane] = bv;
+    Gs[v][lane] = x * LOG2E;
+    Bs[v][lane] = bv;
+    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
     blk.gam[lane] = expf(x);
     blk.tail[lane] = expf(glast - x);
   }
+#pragma unroll
+  for (int r = 0; r < nrt; ++r)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      kf[r][kb] = keep_if<T>(kf[r][kb], 16 * r + i16 < len);
+      qa[r][kb] = keep_if<T>(qa[r][kb], 16 * r + i16 < len);
+    }
 
-  // ---- MP = exp(G_i - G_j) (Q K^T)_ij, j <= i ------------------------------
+  // ---- MP = exp(G_i - G_j) (Q K^T)_ij, j <= i, for every head from one
+  //      Gram tile: lane (g, n) of K_c Q_r^T holds P[16r + n][16c + 4g + q] ----
 #pragma unroll
   for (int r = 0; r < nrt; ++r) {
     f32x4 kq[nrt];
@@ -270,124 +274,144 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
       for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kq[c], kf[c][kb], qa[r][kb]);
     }
     const int i = 16 * r + i16;
-    const float gi = Gs[i];
 #pragma unroll
-    for (int c = 0; c <= r; ++c) {
-      const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[16 * c + 4 * g4]);
+    for (int v = 0; v < HPW; ++v) {
+      const float gi = Gs[v][i];
+      f32x4 mp[nrt];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = 16 * c + 4 * g4 + q;
-        kq[c][q] = j <= i ? fast_exp2(gi - gj[q]) * kq[c][q] : 0.f;
+      for (int c = 0; c <= r; ++c) {
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[v][16 * c + 4 * g4]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = 16 * c + 4 * g4 + q;
+          mp[c][q] = j <= i ? fast_exp2(gi - gj[q]) * kq[c][q] : 0.f;
+        }
+      }
+      Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h0 + v);
+#pragma unroll
+      for (int kb = 0; kb <= r / 2; ++kb) {
+        const f32x4 hi = 2 * kb + 1 <= r ? mp[2 * kb + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        store_frag_native<T>(blk.MP + (tri_idx(r, kb) * 64 + lane) * 8, make_frag<T>(mp[2 * kb], hi));
       }
     }
+  }
 #pragma unroll
-    for (int kb = 0; kb <= r / 2; ++kb) {
-      const f32x4 hi = 2 * kb + 1 <= r ? kq[2 * kb + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
-      store_frag_native<T>(blk.MP + (tri_idx(r, kb) * 64 + lane) * 8, make_frag<T>(kq[2 * kb], hi));
+  for (int v = 0; v < HPW; ++v) {
+    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h0 + v);
+#pragma unroll
+    for (int f = 0; f < NTRI; ++f) {
+      int r, kb;
+      tri_rc(f, r, kb);
+      if (r >= nrt) store_frag_native<T>(blk.MP + (f * 64 + lane) * 8, zero_frag<T>());
     }
   }
-#pragma unroll
-  for (int f = 0; f < NTRI; ++f) {
-    int r, kb;
-    tri_rc(f, r, kb);
-    if (r >= nrt) store_frag_native<T>(blk.MP + (f * 64 + lane) * 8, zero_frag<T>());
-  }
 
-  // ---- L_ij = beta_i exp(G_i - G_j) (K K^T)_ij, j < i: off-diagonal tiles stay
-  //      in registers, diagonal tiles go to LDS for the substitution ------------
-  f32x4 Lt[nrt][nrt];   // [r][c], c < r used
+  // ---- L_ij = beta_i exp(G_i - G_j) (K K^T)_ij, j < i, for every head:
+  //      off-diagonal tiles stay in registers, diagonal tiles go to LDS --------
+  f32x4 Lt[HPW][nrt][nrt];   // [v][r][c], c < r used
 #pragma unroll
   for (int r = 0; r < nrt; ++r) {
-    const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[16 * r + 4 * g4]);
-    const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[16 * r + 4 * g4]);
 #pragma unroll
     for (int c = 0; c <= r; ++c) {
       f32x4 kk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kk, kf[r][kb], kf[c][kb]);
-      const float gj = Gs[16 * c + i16];
-      f32x4 l;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool below = c < r || i16 < 4 * g4 + q;
-        l[q] = below ? bi[q] * fast_exp2(gi[q] - gj) * kk[q] : 0.f;
-      }
-      if (c < r) {
-        Lt[r][c] = l;
-      } else {
+      for (int v = 0; v < HPW; ++v) {
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[v][16 * r + 4 * g4]);
+        const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[v][16 * r + 4 * g4]);
+        const float gj = Gs[v][16 * c + i16];
+        f32x4 l;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) Ld[(r * 16 + 4 * g4 + q) * DS + i16] = l[q];
+        for (int q = 0; q < 4; ++q) {
+          const bool below = c < r || i16 < 4 * g4 + q;
+          l[q] = below ? bi[q] * fast_exp2(gi[q] - gj) * kk[q] : 0.f;
+        }
+        if (c < r) {
+          Lt[v][r][c] = l;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Ld[v][(r * 16 + 4 * g4 + q) * DS + i16] = l[q];
+        }
       }
     }
   }
 
-  // ---- diagonal blocks: lane (b, r) computes row r of (I + L_bb)^-1 by
-  //      back-substitution, X (I + L) = I, over k = 15 .. 1 -------------------
-  {
-    const int b = lane >> 4, r = lane & 15;
-    const float* Lb = Ld + b * 16 * DS;
-    float x[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = (j == r) ? 1.f : 0.f;
+  for (int v = 0; v < HPW; ++v) {
+    // ---- diagonal blocks: lane (b, r) computes row r of (I + L_bb)^-1 by
+    //      back-substitution, X (I + L) = I, over k = 15 .. 1 -----------------
+    {
+      const int b = lane >> 4, r = lane & 15;
+      const float* Lb = Ld[v] + b * 16 * DS;
+      float x[16];
 #pragma unroll
-    for (int k = 15; k >= 1; --k) {
-      const float xk = x[k];
+      for (int j = 0; j < 16; ++j) x[j] = (j == r) ? 1.f : 0.f;
 #pragma unroll
-      for (int j4 = 0; j4 < k; j4 += 4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lb + k * DS + j4);
+      for (int k = 15; k >= 1; --k) {
+        const float xk = x[k];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (j4 + u < k) x[j4 + u] = fmaf(-l4[u], xk, x[j4 + u]);
+        for (int j4 = 0; j4 < k; j4 += 4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lb + k * DS + j4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j4 + u < k) x[j4 + u] = fmaf(-l4[u], xk, x[j4 + u]);
+        }
+      }
+      // the previous head's reads of Xd are complete (LDS is in order per wave)
+      float* xr = Xd + (b * 16 + r) * DS;
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) *reinterpret_cast<f32x4*>(xr + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the whole wave's rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- off-diagonal blocks row by row: Z[i][j] = X_ij^T = -Z_jj sum_k
+    //      L_kj^T Z[i][k]; a finished row goes straight out as A' fragments ---
+    f32x4 Xa[nrt], Zd[nrt];   // X_jj in accumulator layout; Z_jj
+#pragma unroll
+    for (int j = 0; j < nrt; ++j) {
+      const float* xb = Xd + j * 16 * DS;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Xa[j][q] = xb[(4 * g4 + q) * DS + i16];
+      Zd[j] = *reinterpret_cast<const f32x4*>(xb + i16 * DS + 4 * g4);
+    }
+    Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h0 + v);
+#pragma unroll
+    for (int i = 0; i < nrt; ++i) {
+      f32x4 Z[nrt];
+      Z[i] = Zd[i];
+#pragma unroll
+      for (int j = i - 1; j >= 0; --j) {
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = j + 1; k <= i; ++k) mma_tn(P, Lt[v][k][j], Z[k]);
+        f32x4 zij = {0.f, 0.f, 0.f, 0.f};
+        mma_tn(zij, Xa[j], P);
+        Z[j] = -zij;
+      }
+      // A' = X diag(beta): lane (g, n) of Z[j] holds X[16i + n][16j + 4g + q]
+#pragma unroll
+      for (int kb = 0; kb <= i / 2; ++kb) {
+        const int c0 = 2 * kb, c1 = 2 * kb + 1;
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&Bs[v][16 * c0 + 4 * g4]);
+        const f32x4 lo = Z[c0] * b0;
+        f32x4 hi = {0.f, 0.f, 0.f, 0.f};
+        if (c1 <= i) {
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(&Bs[v][16 * c1 + 4 * g4]);
+          hi = Z[c1] * b1;
+        }
+        store_frag_native<T>(blk.A + (tri_idx(i, kb) * 64 + lane) * 8, make_frag<T>(lo, hi));
       }
     }
-    float* xr = Xd + (b * 16 + r) * DS;
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) *reinterpret_cast<f32x4*>(xr + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the whole wave's rows are in LDS
-  __builtin_amdgcn_wave_barrier();
-
-  // ---- off-diagonal blocks, by distance from the diagonal ------------------
-  f32x4 Xa[nrt], Z[nrt][nrt];   // Xa[j]: X_jj in accumulator layout; Z[i][j] = X_ij^T
-#pragma unroll
-  for (int j = 0; j < nrt; ++j) {
-    const float* xb = Xd + j * 16 * DS;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) Xa[j][q] = xb[(4 * g4 + q) * DS + i16];
-    Z[j][j] = *reinterpret_cast<const f32x4*>(xb + i16 * DS + 4 * g4);
-  }
-#pragma unroll
-  for (int d = 1; d < nrt; ++d)
-#pragma unroll
-    for (int j = 0; j + d < nrt; ++j) {
-      const int i = j + d;
-      f32x4 P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = j + 1; k <= i; ++k) mma_tn(P, Lt[k][j], Z[i][k]);
-      f32x4 zij = {0.f, 0.f, 0.f, 0.f};
-      mma_tn(zij, Xa[j], P);
-      Z[i][j] = -zij;
+    for (int f = 0; f < NTRI; ++f) {
+      int r, kb;
+      tri_rc(f, r, kb);
+      if (r >= nrt) store_frag_native<T>(blk.A + (f * 64 + lane) * 8, zero_frag<T>());
     }
-
-  // ---- A' = X diag(beta) in fragment order: lane (g, n) of Z[i][j] holds
-  //      X[16i + n][16j + 4g + q] -----------------------------------------------
-#pragma unroll
-  for (int f = 0; f < NTRI; ++f) {
-    int r, kb;
-    tri_rc(f, r, kb);
-    Frag<T> fr = zero_frag<T>();
-    if (r < nrt) {
-      const int c0 = 2 * kb, c1 = 2 * kb + 1;
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&Bs[16 * c0 + 4 * g4]);
-      const f32x4 lo = Z[r][c0] * b0;
-      f32x4 hi = {0.f, 0.f, 0.f, 0.f};
-      if (c1 <= r) {
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&Bs[16 * c1 + 4 * g4]);
-        hi = Z[r][c1] * b1;
-      }
-      fr = make_frag<T>(lo, hi);
-    }
-    store_frag_native<T>(blk.A + (f * 64 + lane) * 8, fr);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // this head's Xd reads are done before the next head writes it
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -932,11 +956,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 0) {
-    const long long items = (long long)a.max_chunks * a.Hv;
+    // value heads in pairs when pairs share a key head (Hv / Hq even)
+    const bool pairs = ((a.Hv / a.Hq) % 2) == 0;
+    const long long items = (long long)a.max_chunks * (pairs ? a.Hv / 2 : a.Hv);
     const long long blocks = 8 * ((items + 7) / 8);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     prof_begin(K_PREP, st);
-    hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C>), dim3((unsigned)blocks), dim3(64), 0, st, a);
+    if (pairs)
+      hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C, 2>), dim3((unsigned)blocks), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<T, DK, C, 1>), dim3((unsigned)blocks), dim3(64), 0, st, a);
     prof_end(K_PREP, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
