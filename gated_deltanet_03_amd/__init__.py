@@ -28,7 +28,7 @@ GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 _DTYPES = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 EXPORTED = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
-            "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot",
+            "gdn_prefill_chunked_states", "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot",
             "gdn_status_string", "gdn_last_error", "gdn_profile_enable", "gdn_profile_collect")
 
 
@@ -64,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_prefill_chunked.restype = i32
     lib.gdn_prefill_chunked.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]
     lib.gdn_recurrent_step.restype = i32
+    lib.gdn_prefill_chunked_states.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, i64, vp,
+                                               sz, vp]
+    lib.gdn_prefill_chunked_states.restype = i32
     lib.gdn_recurrent_step.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, i32, vp, vp]
     lib.gdn_replay_state_updates.restype = i32
     lib.gdn_replay_state_updates.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -139,6 +142,26 @@ def gdn_prefill_chunked(q, k, v, g, beta, *, scale=None, initial_state=None,
     """Chunked prefill.  Dense q/k [B,T,Hq,dk], v [B,T,Hv,dv], g/beta [B,T,Hv];
     ragged: the same without B (or B=1) plus cu_seqlens int32 [N+1] on the device.
     Returns (o, final_state or None)."""
+    return _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride, cu_seqlens,
+                    chunk_size, o, final_state, output_final_state, workspace, False, None, None)[:2]
+
+
+def gdn_prefill_chunked_states(q, k, v, g, beta, *, scale=None, initial_state=None,
+                               initial_state_batch_stride=None, cu_seqlens=None, chunk_size=64,
+                               o=None, final_state=None, output_final_state=True, workspace=None,
+                               chunk_states=None, num_chunks=None):
+    """Chunked prefill that also returns the state after every chunk:
+    chunk_states [sum_s ceil(L_s / chunk_size), Hv, dk, dv] fp32, sequence s's
+    chunk j at index sum_{s'<s} ceil(L_s'/chunk_size) + j.  Without
+    ``chunk_states`` or ``num_chunks`` the count is taken from the lengths
+    (ragged input: one device-to-host read of cu_seqlens).
+    Returns (o, final_state or None, chunk_states)."""
+    return _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride, cu_seqlens,
+                    chunk_size, o, final_state, output_final_state, workspace, True, chunk_states, num_chunks)
+
+
+def _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride, cu_seqlens, chunk_size,
+             o, final_state, output_final_state, workspace, emit, chunk_states, num_chunks):
     lib = load_library()
     dev = q.device
     sh = _shape_from(q, k, v, scale, cu_seqlens)
@@ -161,11 +184,27 @@ def gdn_prefill_chunked(q, k, v, g, beta, *, scale=None, initial_state=None,
     need = gdn_prefill_workspace_bytes(sh, chunk_size, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _check(lib.gdn_prefill_chunked(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(initial_state), int(initial_state_batch_stride), _ptr(cu_seqlens),
-                                   int(chunk_size), _ptr(o), _ptr(final_state), _ptr(workspace),
-                                   workspace.numel(), _stream(dev)))
-    return o, final_state
+    common = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+              int(initial_state_batch_stride), _ptr(cu_seqlens), int(chunk_size), _ptr(o), _ptr(final_state))
+    if not emit:
+        _check(lib.gdn_prefill_chunked(*common, _ptr(workspace), workspace.numel(), _stream(dev)))
+        return o, final_state, None
+    if chunk_states is None:
+        if num_chunks is None:
+            if cu_seqlens is None:
+                num_chunks = sh.B * (-(-sh.T // chunk_size))
+            else:
+                lens = cu_seqlens.cpu().diff()
+                num_chunks = int(((lens + chunk_size - 1) // chunk_size).sum())
+        # at least one entry, so the buffer has an address even with no chunks
+        buf = torch.empty((max(int(num_chunks), 1), sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+        chunk_states = buf[:int(num_chunks)]
+    else:
+        buf = chunk_states
+    _need(buf, "chunk_states", torch.float32, dev)
+    _check(lib.gdn_prefill_chunked_states(*common, _ptr(buf), int(chunk_states.numel() // max(per, 1)),
+                                          _ptr(workspace), workspace.numel(), _stream(dev)))
+    return o, final_state, chunk_states
 
 
 def gdn_recurrent_step(q, k, v, g, beta, *, scale=None, initial_state=None,
@@ -248,5 +287,6 @@ def gdn_profile_collect() -> dict:
     return {names[i].decode(): (int(cnt[i]), float(ms[i])) for i in range(min(k, n))}
 
 
-__all__ = ["gdn_profile_enable", "gdn_profile_collect", "load_library", "GdnError", "gdn_shape", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
+__all__ = ["gdn_profile_enable", "gdn_profile_collect", "load_library", "GdnError", "gdn_shape",
+           "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_states",
            "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot", "EXPORTED", "LIB_PATH"]

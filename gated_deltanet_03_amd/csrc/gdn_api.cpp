@@ -1,6 +1,7 @@
 // C-ABI entry points of libgdn.so: host-side validation, workspace sizing and
 // dispatch to the HIP kernels.  Validation runs before any HIP call, so a
 // rejected call enqueues nothing (and can be exercised without a GPU).
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -146,10 +147,12 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape* sh, int32_t chunk, int32_t r
   return w.head + (size_t)w.max_chunks * sh->Hv * gdn::chunk_block_bytes((gdn::DType)sh->dtype);
 }
 
-gdn_status gdn_prefill_chunked(const gdn_shape* sh, const void* q, const void* k, const void* v,
+}  // extern "C"
+
+static gdn_status prefill_impl(const gdn_shape* sh, const void* q, const void* k, const void* v,
                                const float* g, const float* beta, const float* s0, int64_t s0_stride,
-                               const int32_t* cu, int32_t chunk, void* o, float* s_out, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               const int32_t* cu, int32_t chunk, void* o, float* s_out, float* cs,
+                               int64_t cs_cap, void* ws, size_t ws_bytes, void* stream, const char* name) {
   int64_t total = 0;
   gdn_status st = check_shape(sh, cu, &total);
   if (st != GDN_OK) return st;
@@ -167,6 +170,25 @@ gdn_status gdn_prefill_chunked(const gdn_shape* sh, const void* q, const void* k
   if (ws == nullptr || ws_bytes < need)
     return fail(GDN_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
   if (!aligned16(ws)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (cs != nullptr) {
+    // no sequence set has more chunks than the workspace bound, so entries
+    // past it are never written and take no part in the overlap check
+    cs_cap = std::min(cs_cap, (int64_t)ws_layout(sh, chunk, total).max_chunks);
+    const size_t per = (size_t)sh->Hv * sh->dk * sh->dv * 4;
+    const size_t cs_bytes = (size_t)cs_cap * per;
+    if (!aligned16(cs)) return fail(GDN_ERR_INVALID_ARG, "chunk_states is not 16-byte aligned");
+    const size_t es = elem_size(sh->dtype);
+    const size_t tb = (size_t)total;
+    const void* bufs[9] = {q, k, v, g, beta, o, s0, s_out, ws};
+    const size_t lens[9] = {tb * sh->Hq * sh->dk * es, tb * sh->Hq * sh->dk * es, tb * sh->Hv * sh->dv * es,
+                            tb * sh->Hv * 4, tb * sh->Hv * 4, tb * sh->Hv * sh->dv * es,
+                            s0 ? ((size_t)(sh->B - 1) * (size_t)s0_stride * 4 + per) : 0,
+                            s_out ? (size_t)sh->B * per : 0, ws_bytes};
+    const char* names[9] = {"q", "k", "v", "g", "beta", "o", "initial_state", "final_state", "workspace"};
+    for (int i = 0; i < 9; ++i)
+      if (bufs[i] != nullptr && overlaps(cs, cs_bytes, bufs[i], lens[i]))
+        return fail(GDN_ERR_INVALID_ARG, "chunk_states overlaps %s", names[i]);
+  }
   if (total == 0 && s_out == nullptr) return GDN_OK;
 
   gdn::PrefillArgs a{};
@@ -182,9 +204,31 @@ gdn_status gdn_prefill_chunked(const gdn_shape* sh, const void* q, const void* k
   a.chunk_offsets = static_cast<int32_t*>(ws);
   a.chunk_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.info_off);
   a.chunk_data = static_cast<char*>(ws) + w.head;
+  a.chunk_states = cs;
+  a.chunk_states_cap = cs != nullptr ? cs_cap : 0;
   hipError_t e = gdn::launch_prefill((gdn::DType)sh->dtype, a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");
+  if (e != hipSuccess) return hip_fail(e, name);
   return GDN_OK;
+}
+
+extern "C" {
+
+gdn_status gdn_prefill_chunked(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const float* s0, int64_t s0_stride,
+                               const int32_t* cu, int32_t chunk, void* o, float* s_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return prefill_impl(sh, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, nullptr, 0, ws, ws_bytes, stream,
+                      "gdn_prefill_chunked launch");
+}
+
+gdn_status gdn_prefill_chunked_states(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                                      const float* g, const float* beta, const float* s0, int64_t s0_stride,
+                                      const int32_t* cu, int32_t chunk, void* o, float* s_out, float* cs,
+                                      int64_t cs_cap, void* ws, size_t ws_bytes, void* stream) {
+  if (cs == nullptr) return fail(GDN_ERR_INVALID_ARG, "chunk_states is NULL");
+  if (cs_cap < 0) return fail(GDN_ERR_INVALID_ARG, "chunk_states_capacity=%lld < 0", (long long)cs_cap);
+  return prefill_impl(sh, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, cs, cs_cap, ws, ws_bytes, stream,
+                      "gdn_prefill_chunked_states launch");
 }
 
 gdn_status gdn_recurrent_step(const gdn_shape* sh, const void* q, const void* k, const void* v,

@@ -57,6 +57,8 @@ struct PrefillArgs {
   int32_t* chunk_offsets;   // [B+1] inside the workspace
   int32_t* chunk_info;      // [max_chunks][2]: first token, length (0 past the last chunk)
   void* chunk_data;         // per (chunk, value head) blocks inside the workspace
+  float* chunk_states;      // NULL, or [chunk_states_cap, Hv, dk, dv]: state after each chunk
+  int64_t chunk_states_cap;
 };
 
 // Per (chunk, value head) workspace block written by the chunk-prep kernel:

@@ -487,7 +487,7 @@ struct StateSmem {
   static constexpr int OK_ = 0, OQ = KB, OV = 2 * KB, OA = 2 * KB + VB, OG = 2 * KB + VB + AB;
 };
 
-template <typename T, int DK, int C, int NG, int NDW>
+template <typename T, int DK, int C, int NG, int NDW, bool EMIT>
 __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(PrefillArgs p) {
   using SM = StateSmem<T, DK, NG>;
   constexpr int SW = SM::SW;
@@ -863,6 +863,21 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
         store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
       }
+      if constexpr (EMIT) {
+        // the state after this chunk's last token, in the [dk, dv] state layout:
+        // a wave-uniform row base per store plus one per-lane 32-bit offset
+        if (active && (int64_t)(cbeg + c) < p.chunk_states_cap) {
+          float* cs = p.chunk_states + ((size_t)(cbeg + c) * p.Hv + h) * DK * dv;
+          const int lo = (DK < 32 ? 4 * g4 : 8 * g4) * dv + col0 + i16;
+#pragma unroll
+          for (int r = 0; r < NST; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = perm_dk<DK>(16 * r + q);          // lane group 0's row
+              (cs + (size_t)row * dv)[lo] = S[r][q];
+            }
+        }
+      }
     } else if (!dmaw) {
       // ---- O = scale (gamma QS + MP Delta) -> o -----------------------------------
       const Frag<T> Db0 = load_frag_native<T>(dx_mine), Db1 = load_frag_native<T>(dx_mine + 512);
@@ -925,14 +940,14 @@ static int device_cus() {
   return cached[dev];
 }
 
-template <typename T, int DK, int C, int NG, int NDW>
+template <typename T, int DK, int C, int NG, int NDW, bool EMIT>
 static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
   using SM = StateSmem<T, DK, NG>;
   const size_t sm2 = SM::total;
   if (sm2 > 160 * 1024) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C, NG, NDW>,
+    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C, NG, NDW, EMIT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
     if (e != hipSuccess) return e;
     attr = true;
@@ -942,7 +957,7 @@ static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
   const long long sblocks = 8LL * nslices * (a.Hv / a.Hq) * ((groups + 7) / 8);
   if (sblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   prof_begin(K_STATE, st);
-  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C, NG, NDW>), dim3((unsigned)sblocks), dim3(64 * (2 * NG + NDW)),
+  hipLaunchKernelGGL((chunk_state_kernel<T, DK, C, NG, NDW, EMIT>), dim3((unsigned)sblocks), dim3(64 * (2 * NG + NDW)),
                      sm2, st, a);
   prof_end(K_STATE, st);
   return hipGetLastError();
@@ -973,10 +988,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   // more CUs and halves the LDS and load traffic per CU per chunk, which
   // shortens the sequential chunk step; 4 (64 columns, 8 waves) is kept for
   // batches with more (sequence, head, slice) work than two workgroups per CU.
+  // The chunk-boundary state stores live in a separate instantiation so that
+  // the plain prefill keeps its register allocation.
+  const bool emit = a.chunk_states != nullptr;
   if ((long long)a.B * a.Hv * ((a.dv + 31) / 32) <= 2LL * device_cus())
-    e = launch_state<T, DK, C, 2, 2>(a, st);   // 6 waves: + two load-issuing waves
+    e = emit ? launch_state<T, DK, C, 2, 2, true>(a, st)    // 6 waves: + two load-issuing waves
+             : launch_state<T, DK, C, 2, 2, false>(a, st);
   else
-    e = launch_state<T, DK, C, 4, 0>(a, st);   // 8 waves: the chain waves issue the loads
+    e = emit ? launch_state<T, DK, C, 4, 0, true>(a, st)    // 8 waves: the chain waves issue the loads
+             : launch_state<T, DK, C, 4, 0, false>(a, st);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

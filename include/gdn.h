@@ -117,6 +117,36 @@ gdn_status gdn_prefill_chunked(const gdn_shape* shape, const void* q, const void
                                void* stream);
 
 /*
+ * Chunked prefill that also emits the state at every chunk boundary
+ * [executorch issue 23097, "Work to cover": GDN chunk boundaries, prefix
+ * snapshots retained in device memory and reused; executorch issue 23099,
+ * "Work to cover": the reused prefix stays unchanged].  A boundary state is a
+ * ready-made snapshot of the prefix that ends there: passing it as
+ * `initial_state` of a later call continues the sequence from that point.
+ *
+ * Same arguments, results and errors as gdn_prefill_chunked, plus
+ *  chunk_states           [num_chunks, Hv, dk, dv] fp32, device, 16-byte
+ *                         aligned, not NULL.  Sequence s has
+ *                         n_s = ceil(L_s / chunk_size) chunks (0 when empty);
+ *                         its chunk j has index sum_{s' < s} n_s' + j (dense
+ *                         input: s * ceil(T / chunk_size) + j) and receives the
+ *                         state after the first min((j+1)*chunk_size, L_s)
+ *                         tokens of s, so each sequence's last entry equals its
+ *                         final state.  Must not overlap any other buffer.
+ *  chunk_states_capacity  entries available (>= 0); chunks with an index at
+ *                         or beyond it are not written (size it to
+ *                         sum_s n_s to receive them all).
+ * Costs one extra fp32 state write per (chunk, value head).
+ */
+gdn_status gdn_prefill_chunked_states(const gdn_shape* shape, const void* q, const void* k,
+                                      const void* v, const float* g, const float* beta,
+                                      const float* initial_state, int64_t initial_state_batch_stride,
+                                      const int32_t* cu_seqlens, int32_t chunk_size, void* o,
+                                      float* final_state, float* chunk_states,
+                                      int64_t chunk_states_capacity, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * Recurrent step with compact state-update capture [onnxruntime PR 32767,
  * "Changes": state_update_capacity, the required [batch] capture_count input,
  * the packed float32 state_update output, clamped per-row prefix capture,

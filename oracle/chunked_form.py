@@ -38,7 +38,9 @@ def chunked(q, k, v, g, beta, scale, Hq, Hv, chunk, cu_seqlens=None, num_seqs=No
     s0 = _f64(initial_state)
     o = np.zeros((Ttot, Hv, dv))
     final = np.zeros((N, Hv, dk, dv))
+    boundary = []                     # state after each chunk, in sequence order
     for s, (t0, t1) in enumerate(bounds):
+        sb = np.zeros((-(-(t1 - t0) // chunk), Hv, dk, dv))
         for h in range(Hv):
             hk = h // G
             S = np.zeros((dk, dv)) if s0 is None else s0[s, h].copy()
@@ -56,5 +58,8 @@ def chunked(q, k, v, g, beta, scale, Hq, Hv, chunk, cu_seqlens=None, num_seqs=No
                 o[c0:c1, h] = scale * (np.exp(Gc)[:, None] * (Q @ S) + (Mc * (Q @ K.T)) @ Delta)
                 Kt = np.exp(Gc[-1] - Gc)[:, None] * K
                 S = np.exp(Gc[-1]) * S + Kt.T @ Delta
+                sb[(c0 - t0) // chunk, h] = S
             final[s, h] = S
-    return {"o": o, "final": final}
+        boundary.append(sb)
+    return {"o": o, "final": final,
+            "boundary": np.concatenate(boundary) if boundary else np.zeros((0, Hv, dk, dv))}

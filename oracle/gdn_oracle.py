@@ -88,7 +88,7 @@ def _token_update(S, a, kt, vt, b, qt, scale):
 
 
 def recurrent(q, k, v, g, beta, scale, Hq, Hv, cu_seqlens=None, num_seqs=None,
-              initial_state=None, initial_state_broadcast=False, heads=None):
+              initial_state=None, initial_state_broadcast=False, heads=None, boundary_every=None):
     """Run the recurrence over every sequence, token by token.
 
     Layouts (packed tokens): q, k [Ttot, Hq, dk]; v [Ttot, Hv, dv]; g, beta
@@ -97,11 +97,18 @@ def recurrent(q, k, v, g, beta, scale, Hq, Hv, cu_seqlens=None, num_seqs=None,
     ``initial_state_broadcast``); None means zeros.  ``heads`` restricts the
     computation to a subset of value heads (sampled parity at large sizes).
 
+    ``boundary_every`` = C also records the state after every C-th token of
+    each sequence and after its last token, i.e. the snapshot of every prefix
+    that ends on a chunk boundary ([executorch issue 23097, "Work to cover"]:
+    GDN chunk boundaries and retained prefix snapshots).  Sequence s
+    contributes ceil(L_s / C) entries, in sequence order.
+
     Returns dict with
-      o      [Ttot, Hv, dv]   (entries of heads not computed are NaN)
-      final  [N, Hv, dk, dv]
-      alpha  [Ttot, Hv]       per-token decay exp(g)
-      delta  [Ttot, Hv, dv]   per-token delta (includes beta)
+      o        [Ttot, Hv, dv]   (entries of heads not computed are NaN)
+      final    [N, Hv, dk, dv]
+      alpha    [Ttot, Hv]       per-token decay exp(g)
+      delta    [Ttot, Hv, dv]   per-token delta (includes beta)
+      boundary [sum_s ceil(L_s/C), Hv, dk, dv] (only with ``boundary_every``)
     """
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     Ttot, _, dk = k.shape
@@ -124,6 +131,7 @@ def recurrent(q, k, v, g, beta, scale, Hq, Hv, cu_seqlens=None, num_seqs=None,
     final = np.full((N, Hv, dk, dv), np.nan)
     alpha_all = np.full((Ttot, Hv), np.nan)
     delta_all = np.full((Ttot, Hv, dv), np.nan)
+    boundary = []
     for s, (t0, t1) in enumerate(bounds):
         if s0 is None:
             S = np.zeros((len(hs), dk, dv))
@@ -135,8 +143,15 @@ def recurrent(q, k, v, g, beta, scale, Hq, Hv, cu_seqlens=None, num_seqs=None,
             o[t, hs] = o_t
             alpha_all[t, hs] = a
             delta_all[t, hs] = d_t
+            if boundary_every and ((t + 1 - t0) % boundary_every == 0 or t == t1 - 1):
+                snap = np.full((Hv, dk, dv), np.nan)
+                snap[hs] = S
+                boundary.append(snap)
         final[s, hs] = S
-    return {"o": o, "final": final, "alpha": alpha_all, "delta": delta_all}
+    out = {"o": o, "final": final, "alpha": alpha_all, "delta": delta_all}
+    if boundary_every:
+        out["boundary"] = np.stack(boundary) if boundary else np.zeros((0, Hv, dk, dv))
+    return out
 
 
 def capture(k, alpha, delta, Hq, Hv, capacity, capture_count, active,

@@ -114,6 +114,25 @@ def test_workspace_validation_and_sizing(lib):
     assert prefill(lib, sh, ws=ctypes.c_void_p(0x40000008), wsb=need) == gdn.GDN_ERR_INVALID_ARG
 
 
+def test_chunk_states_validation(lib):
+    sh = shape()
+    ws = ctypes.c_void_p(0x40000000)
+    wsb = gdn.gdn_prefill_workspace_bytes(sh, 64, False)
+
+    def call(cs, cap):
+        return lib.gdn_prefill_chunked_states(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL, 64,
+                                              ctypes.c_void_p(0x900000), NULL, cs, cap, ws, wsb, NULL)
+    assert call(NULL, 4) == gdn.GDN_ERR_INVALID_ARG and "chunk_states is NULL" in last(lib)
+    assert call(ctypes.c_void_p(0x80000000), -1) == gdn.GDN_ERR_INVALID_ARG
+    assert call(ctypes.c_void_p(0x80000008), 4) == gdn.GDN_ERR_INVALID_ARG and "aligned" in last(lib)
+    # overlapping the workspace, o, or an input
+    assert call(ctypes.c_void_p(0x40000000 + 256), 4) == gdn.GDN_ERR_INVALID_ARG and "workspace" in last(lib)
+    assert call(ctypes.c_void_p(0x900000), 4) == gdn.GDN_ERR_INVALID_ARG and "overlaps o" in last(lib)
+    assert call(FAKE, 4) == gdn.GDN_ERR_INVALID_ARG and "overlaps" in last(lib)
+    # a huge capacity is clamped to the chunk bound (no size overflow) and still overlap-checked
+    assert call(ctypes.c_void_p(0x40000000 - 1024), 1 << 60) == gdn.GDN_ERR_INVALID_ARG and "workspace" in last(lib)
+
+
 def test_replay_and_snapshot_validation(lib):
     assert lib.gdn_replay_state_updates(2, 2, 5, 128, 128, 7, FAKE, FAKE, FAKE, NULL) == gdn.GDN_ERR_INVALID_ARG
     assert lib.gdn_replay_state_updates(2, 2, 4, 128, 128, -1, FAKE, FAKE, FAKE, NULL) == gdn.GDN_ERR_INVALID_ARG

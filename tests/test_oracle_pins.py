@@ -228,6 +228,45 @@ def test_varlen_equals_independent_runs_and_empty_sequence():
     np.testing.assert_array_equal(rb["final"], re["final"])
 
 
+def test_chunk_boundary_states():
+    """The recorded boundary states are the states of the prefixes that end on
+    chunk boundaries: with beta = 0 the state after m tokens is the closed form
+    exp(sum_{t<m} g_t) S0 (an off-by-one in the recording position changes the
+    exponent); for generic inputs the entries equal the chunk-end states of the
+    chunked form (a different algorithm), each sequence's last entry equals its
+    final state, and an entry equals a separate run over that prefix."""
+    rng = np.random.default_rng(24)
+    lengths = [10, 0, 4, 1, 8]
+    C = 4
+    T = sum(lengths)
+    Hq, Hv, dk, dv = 1, 2, 3, 2
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k, v, g, _ = _case(rng, T, Hq, Hv, dk, dv)
+    S0 = rng.standard_normal((len(lengths), Hv, dk, dv))
+    r = oracle.recurrent(q, k, v, g, np.zeros((T, Hv)), 0.5, Hq, Hv, cu_seqlens=cu, initial_state=S0,
+                         boundary_every=C)
+    counts = [-(-L // C) for L in lengths]
+    assert r["boundary"].shape == (sum(counts), Hv, dk, dv)
+    i = 0
+    for s, L in enumerate(lengths):
+        for j in range(counts[s]):
+            m = min((j + 1) * C, L)
+            decay = np.exp(g[cu[s]:cu[s] + m].sum(axis=0))              # [Hv]
+            np.testing.assert_allclose(r["boundary"][i], decay[:, None, None] * S0[s], rtol=1e-13)
+            i += 1
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T, Hv))))
+    r = oracle.recurrent(q, k, v, g, beta, 0.5, Hq, Hv, cu_seqlens=cu, initial_state=S0, boundary_every=C)
+    c = oracle.chunked(q, k, v, g, beta, 0.5, Hq, Hv, C, cu_seqlens=cu, initial_state=S0)
+    np.testing.assert_allclose(r["boundary"], c["boundary"], atol=1e-12)
+    last = np.cumsum(counts) - 1
+    for s, L in enumerate(lengths):
+        if L:
+            np.testing.assert_array_equal(r["boundary"][last[s]], r["final"][s])
+    # entry 1 of sequence 0 = the state after its first 8 tokens
+    p = oracle.recurrent(q[:8], k[:8], v[:8], g[:8], beta[:8], 0.5, Hq, Hv, initial_state=S0[:1])
+    np.testing.assert_allclose(r["boundary"][1], p["final"][0], atol=1e-14)
+
+
 def test_shared_key_heads_equal_single_head_runs():
     rng = np.random.default_rng(23)
     T, Hq, Hv, dk, dv = 11, 2, 6, 5, 4
