@@ -28,8 +28,32 @@ GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 _DTYPES = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 EXPORTED = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
-            "gdn_prefill_chunked_states", "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot",
+            "gdn_prefill_chunked_states", "gdn_prefill_chunked_ex", "gdn_recurrent_step",
+            "gdn_recurrent_step_ex", "gdn_replay_state_updates", "gdn_state_snapshot",
             "gdn_status_string", "gdn_last_error", "gdn_profile_enable", "gdn_profile_collect")
+
+
+class gdn_prologue(ctypes.Structure):
+    _fields_ = [("qk_l2norm", ctypes.c_int32), ("qk_l2norm_eps", ctypes.c_float),
+                ("beta_is_logit", ctypes.c_int32), ("gate_A_log", ctypes.c_void_p),
+                ("gate_dt_bias", ctypes.c_void_p)]
+
+
+class Prologue:
+    """Input prologue of the *_ex calls: qk_l2norm (with eps), beta given as
+    logits, and the gate -exp(A_log[h]) * softplus(g + dt_bias[h]) when A_log
+    (fp32 [Hv] on the device) is set.  Tensors are kept alive by this object."""
+
+    def __init__(self, qk_l2norm=False, eps=1e-6, beta_is_logit=False, A_log=None, dt_bias=None):
+        self.qk_l2norm, self.eps, self.beta_is_logit = bool(qk_l2norm), float(eps), bool(beta_is_logit)
+        self.A_log, self.dt_bias = A_log, dt_bias
+
+    def as_c(self, device):
+        for t, n in ((self.A_log, "A_log"), (self.dt_bias, "dt_bias")):
+            _need(t, n, torch.float32, device)
+        return gdn_prologue(int(self.qk_l2norm), self.eps, int(self.beta_is_logit),
+                            None if self.A_log is None else self.A_log.data_ptr(),
+                            None if self.dt_bias is None else self.dt_bias.data_ptr())
 
 
 class gdn_shape(ctypes.Structure):
@@ -67,6 +91,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_prefill_chunked_states.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, i64, vp,
                                                sz, vp]
     lib.gdn_prefill_chunked_states.restype = i32
+    pro = ctypes.POINTER(gdn_prologue)
+    lib.gdn_prefill_chunked_ex.argtypes = [shp, pro, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, i64, vp,
+                                           sz, vp]
+    lib.gdn_prefill_chunked_ex.restype = i32
+    lib.gdn_recurrent_step_ex.argtypes = [shp, pro, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, i32, vp, vp]
+    lib.gdn_recurrent_step_ex.restype = i32
     lib.gdn_recurrent_step.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, i32, vp, vp]
     lib.gdn_replay_state_updates.restype = i32
     lib.gdn_replay_state_updates.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -160,8 +190,21 @@ def gdn_prefill_chunked_states(q, k, v, g, beta, *, scale=None, initial_state=No
                     chunk_size, o, final_state, output_final_state, workspace, True, chunk_states, num_chunks)
 
 
+def gdn_prefill_chunked_ex(q, k, v, g, beta, *, prologue=None, scale=None, initial_state=None,
+                           initial_state_batch_stride=None, cu_seqlens=None, chunk_size=64, o=None,
+                           final_state=None, output_final_state=True, workspace=None, chunk_states=None,
+                           num_chunks=None, emit_chunk_states=False):
+    """Chunked prefill with the input prologue (a ``Prologue`` or None) and,
+    with ``emit_chunk_states`` (or a ``chunk_states`` buffer), the boundary
+    states.  Returns (o, final_state or None, chunk_states or None)."""
+    emit = emit_chunk_states or chunk_states is not None or num_chunks is not None
+    return _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride, cu_seqlens,
+                    chunk_size, o, final_state, output_final_state, workspace, emit, chunk_states, num_chunks,
+                    prologue=prologue if prologue is not None else Prologue())
+
+
 def _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride, cu_seqlens, chunk_size,
-             o, final_state, output_final_state, workspace, emit, chunk_states, num_chunks):
+             o, final_state, output_final_state, workspace, emit, chunk_states, num_chunks, prologue=None):
     lib = load_library()
     dev = q.device
     sh = _shape_from(q, k, v, scale, cu_seqlens)
@@ -186,31 +229,50 @@ def _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     common = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
               int(initial_state_batch_stride), _ptr(cu_seqlens), int(chunk_size), _ptr(o), _ptr(final_state))
+    if prologue is not None:
+        pc = prologue.as_c(dev)
+        buf = None
+        if emit:
+            chunk_states, buf = _chunk_buffer(sh, cu_seqlens, chunk_size, chunk_states, num_chunks, dev)
+        ncs = 0 if buf is None else int(chunk_states.numel() // max(per, 1))
+        _check(lib.gdn_prefill_chunked_ex(common[0], ctypes.byref(pc), *common[1:], _ptr(buf), ncs,
+                                          _ptr(workspace), workspace.numel(), _stream(dev)))
+        return o, final_state, chunk_states if emit else None
     if not emit:
         _check(lib.gdn_prefill_chunked(*common, _ptr(workspace), workspace.numel(), _stream(dev)))
         return o, final_state, None
-    if chunk_states is None:
-        if num_chunks is None:
-            if cu_seqlens is None:
-                num_chunks = sh.B * (-(-sh.T // chunk_size))
-            else:
-                lens = cu_seqlens.cpu().diff()
-                num_chunks = int(((lens + chunk_size - 1) // chunk_size).sum())
-        # at least one entry, so the buffer has an address even with no chunks
-        buf = torch.empty((max(int(num_chunks), 1), sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
-        chunk_states = buf[:int(num_chunks)]
-    else:
-        buf = chunk_states
-    _need(buf, "chunk_states", torch.float32, dev)
+    chunk_states, buf = _chunk_buffer(sh, cu_seqlens, chunk_size, chunk_states, num_chunks, dev)
     _check(lib.gdn_prefill_chunked_states(*common, _ptr(buf), int(chunk_states.numel() // max(per, 1)),
                                           _ptr(workspace), workspace.numel(), _stream(dev)))
     return o, final_state, chunk_states
 
 
+def _chunk_buffer(sh, cu_seqlens, chunk_size, chunk_states, num_chunks, dev):
+    """(chunk_states view, buffer with an address) for the boundary states."""
+    if chunk_states is not None:
+        _need(chunk_states, "chunk_states", torch.float32, dev)
+        return chunk_states, chunk_states
+    if num_chunks is None:
+        if cu_seqlens is None:
+            num_chunks = sh.B * (-(-sh.T // chunk_size))
+        else:
+            lens = cu_seqlens.cpu().diff()
+            num_chunks = int(((lens + chunk_size - 1) // chunk_size).sum())
+    # at least one entry, so the buffer has an address even with no chunks
+    buf = torch.empty((max(int(num_chunks), 1), sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+    return buf[:int(num_chunks)], buf
+
+
+def gdn_recurrent_step_ex(q, k, v, g, beta, *, prologue=None, **kw):
+    """Recurrent step with the input prologue (a ``Prologue`` or None); the
+    other arguments as gdn_recurrent_step.  Returns (o, final_state, state_update)."""
+    return gdn_recurrent_step(q, k, v, g, beta, _prologue=prologue if prologue is not None else Prologue(), **kw)
+
+
 def gdn_recurrent_step(q, k, v, g, beta, *, scale=None, initial_state=None,
                        initial_state_batch_stride=None, cu_seqlens=None, o=None, final_state=None,
                        output_final_state=True, state_update_capacity=0, capture_count=None,
-                       state_update_active=1, state_update=None):
+                       state_update_active=1, state_update=None, _prologue=None):
     """Recurrent step with optional compact capture.  Returns (o, final_state, state_update)."""
     lib = load_library()
     dev = q.device
@@ -237,10 +299,14 @@ def gdn_recurrent_step(q, k, v, g, beta, *, scale=None, initial_state=None,
         R = sh.Hv + sh.Hq * sh.dk + sh.Hv * sh.dv
         state_update = torch.empty((sh.B, cap, R), dtype=torch.float32, device=dev)
     _need(state_update, "state_update", torch.float32, dev)
-    _check(lib.gdn_recurrent_step(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(initial_state), int(initial_state_batch_stride), _ptr(cu_seqlens),
-                                  _ptr(o), _ptr(final_state), cap, _ptr(capture_count),
-                                  int(state_update_active), _ptr(state_update), _stream(dev)))
+    rest = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), int(initial_state_batch_stride),
+            _ptr(cu_seqlens), _ptr(o), _ptr(final_state), cap, _ptr(capture_count), int(state_update_active),
+            _ptr(state_update), _stream(dev))
+    if _prologue is None:
+        _check(lib.gdn_recurrent_step(ctypes.byref(sh), *rest))
+    else:
+        pc = _prologue.as_c(dev)
+        _check(lib.gdn_recurrent_step_ex(ctypes.byref(sh), ctypes.byref(pc), *rest))
     return o, final_state, state_update
 
 
@@ -289,4 +355,5 @@ def gdn_profile_collect() -> dict:
 
 __all__ = ["gdn_profile_enable", "gdn_profile_collect", "load_library", "GdnError", "gdn_shape",
            "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_states",
+           "gdn_prefill_chunked_ex", "gdn_recurrent_step_ex", "Prologue", "gdn_prologue",
            "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot", "EXPORTED", "LIB_PATH"]

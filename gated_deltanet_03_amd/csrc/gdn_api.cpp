@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -105,6 +106,25 @@ gdn_status check_states(const gdn_shape* sh, const float* s0, int64_t stride, co
   return GDN_OK;
 }
 
+gdn_status check_prologue(const gdn_prologue* pr, gdn::Prologue* out) {
+  *out = gdn::Prologue{};
+  if (pr == nullptr) return GDN_OK;
+  if (pr->qk_l2norm != 0) {
+    if (!(pr->qk_l2norm_eps >= 0.f) || pr->qk_l2norm_eps == INFINITY)
+      return fail(GDN_ERR_INVALID_ARG, "qk_l2norm_eps must be finite and >= 0");
+    out->l2norm = 1;
+    out->eps = pr->qk_l2norm_eps;
+  }
+  out->beta_logit = pr->beta_is_logit != 0;
+  if (pr->gate_dt_bias != nullptr && pr->gate_A_log == nullptr)
+    return fail(GDN_ERR_INVALID_ARG, "gate_dt_bias is given without gate_A_log");
+  if ((reinterpret_cast<uintptr_t>(pr->gate_A_log) | reinterpret_cast<uintptr_t>(pr->gate_dt_bias)) & 3u)
+    return fail(GDN_ERR_INVALID_ARG, "gate_A_log / gate_dt_bias are not 4-byte aligned");
+  out->A_log = pr->gate_A_log;
+  out->dt_bias = pr->gate_dt_bias;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,13 +169,16 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape* sh, int32_t chunk, int32_t r
 
 }  // extern "C"
 
-static gdn_status prefill_impl(const gdn_shape* sh, const void* q, const void* k, const void* v,
-                               const float* g, const float* beta, const float* s0, int64_t s0_stride,
-                               const int32_t* cu, int32_t chunk, void* o, float* s_out, float* cs,
-                               int64_t cs_cap, void* ws, size_t ws_bytes, void* stream, const char* name) {
+static gdn_status prefill_impl(const gdn_shape* sh, const gdn_prologue* pro, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, const float* s0,
+                               int64_t s0_stride, const int32_t* cu, int32_t chunk, void* o, float* s_out,
+                               float* cs, int64_t cs_cap, void* ws, size_t ws_bytes, void* stream,
+                               const char* name) {
   int64_t total = 0;
   gdn_status st = check_shape(sh, cu, &total);
   if (st != GDN_OK) return st;
+  gdn::Prologue pr;
+  if ((st = check_prologue(pro, &pr)) != GDN_OK) return st;
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d: supported chunk sizes are 16, 32, 64", chunk);
   if (sh->dtype == GDN_F32 && sh->dk > 64)
@@ -206,6 +229,7 @@ static gdn_status prefill_impl(const gdn_shape* sh, const void* q, const void* k
   a.chunk_data = static_cast<char*>(ws) + w.head;
   a.chunk_states = cs;
   a.chunk_states_cap = cs != nullptr ? cs_cap : 0;
+  a.pro = pr;
   hipError_t e = gdn::launch_prefill((gdn::DType)sh->dtype, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, name);
   return GDN_OK;
@@ -217,8 +241,8 @@ gdn_status gdn_prefill_chunked(const gdn_shape* sh, const void* q, const void* k
                                const float* g, const float* beta, const float* s0, int64_t s0_stride,
                                const int32_t* cu, int32_t chunk, void* o, float* s_out, void* ws,
                                size_t ws_bytes, void* stream) {
-  return prefill_impl(sh, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, nullptr, 0, ws, ws_bytes, stream,
-                      "gdn_prefill_chunked launch");
+  return prefill_impl(sh, nullptr, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, nullptr, 0, ws, ws_bytes,
+                      stream, "gdn_prefill_chunked launch");
 }
 
 gdn_status gdn_prefill_chunked_states(const gdn_shape* sh, const void* q, const void* k, const void* v,
@@ -227,17 +251,31 @@ gdn_status gdn_prefill_chunked_states(const gdn_shape* sh, const void* q, const 
                                       int64_t cs_cap, void* ws, size_t ws_bytes, void* stream) {
   if (cs == nullptr) return fail(GDN_ERR_INVALID_ARG, "chunk_states is NULL");
   if (cs_cap < 0) return fail(GDN_ERR_INVALID_ARG, "chunk_states_capacity=%lld < 0", (long long)cs_cap);
-  return prefill_impl(sh, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, cs, cs_cap, ws, ws_bytes, stream,
-                      "gdn_prefill_chunked_states launch");
+  return prefill_impl(sh, nullptr, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, cs, cs_cap, ws, ws_bytes,
+                      stream, "gdn_prefill_chunked_states launch");
 }
 
-gdn_status gdn_recurrent_step(const gdn_shape* sh, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, const float* s0, int64_t s0_stride,
-                              const int32_t* cu, void* o, float* s_out, int32_t cap, const int32_t* counts,
-                              int32_t active, float* su, void* stream) {
+gdn_status gdn_prefill_chunked_ex(const gdn_shape* sh, const gdn_prologue* pro, const void* q, const void* k,
+                                  const void* v, const float* g, const float* beta, const float* s0,
+                                  int64_t s0_stride, const int32_t* cu, int32_t chunk, void* o, float* s_out,
+                                  float* cs, int64_t cs_cap, void* ws, size_t ws_bytes, void* stream) {
+  if (cs != nullptr && cs_cap < 0)
+    return fail(GDN_ERR_INVALID_ARG, "chunk_states_capacity=%lld < 0", (long long)cs_cap);
+  return prefill_impl(sh, pro, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, cs, cs_cap, ws, ws_bytes,
+                      stream, "gdn_prefill_chunked_ex launch");
+}
+
+}  // extern "C"
+
+static gdn_status recurrent_impl(const gdn_shape* sh, const gdn_prologue* pro, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta, const float* s0,
+                                 int64_t s0_stride, const int32_t* cu, void* o, float* s_out, int32_t cap,
+                                 const int32_t* counts, int32_t active, float* su, void* stream, const char* name) {
   int64_t total = 0;
   gdn_status st = check_shape(sh, cu, &total);
   if (st != GDN_OK) return st;
+  gdn::Prologue pr;
+  if ((st = check_prologue(pro, &pr)) != GDN_OK) return st;
   if ((st = check_tokens(sh, total, q, k, v, g, beta, o)) != GDN_OK) return st;
   if ((st = check_states(sh, s0, s0_stride, s_out)) != GDN_OK) return st;
   if (cap < 0) return fail(GDN_ERR_INVALID_ARG, "state_update_capacity=%d < 0", cap);
@@ -268,9 +306,28 @@ gdn_status gdn_recurrent_step(const gdn_shape* sh, const void* q, const void* k,
   a.B = sh->B; a.T = sh->T; a.total = (int32_t)total;
   a.Hq = sh->Hq; a.Hv = sh->Hv; a.dk = sh->dk; a.dv = sh->dv; a.scale = sh->scale;
   a.cap = cap; a.counts = counts; a.active = active; a.su = su;
+  a.pro = pr;
   hipError_t e = gdn::launch_recurrent((gdn::DType)sh->dtype, a, s);
-  if (e != hipSuccess) return hip_fail(e, "gdn_recurrent_step launch");
+  if (e != hipSuccess) return hip_fail(e, name);
   return GDN_OK;
+}
+
+extern "C" {
+
+gdn_status gdn_recurrent_step(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* s0, int64_t s0_stride,
+                              const int32_t* cu, void* o, float* s_out, int32_t cap, const int32_t* counts,
+                              int32_t active, float* su, void* stream) {
+  return recurrent_impl(sh, nullptr, q, k, v, g, beta, s0, s0_stride, cu, o, s_out, cap, counts, active, su, stream,
+                        "gdn_recurrent_step launch");
+}
+
+gdn_status gdn_recurrent_step_ex(const gdn_shape* sh, const gdn_prologue* pro, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta, const float* s0,
+                                 int64_t s0_stride, const int32_t* cu, void* o, float* s_out, int32_t cap,
+                                 const int32_t* counts, int32_t active, float* su, void* stream) {
+  return recurrent_impl(sh, pro, q, k, v, g, beta, s0, s0_stride, cu, o, s_out, cap, counts, active, su, stream,
+                        "gdn_recurrent_step_ex launch");
 }
 
 gdn_status gdn_replay_state_updates(int32_t B, int32_t Hq, int32_t Hv, int32_t dk, int32_t dv, int32_t cap,

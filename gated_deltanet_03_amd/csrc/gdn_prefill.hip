@@ -108,16 +108,46 @@ template <typename T>
 struct Block {  // views of one (chunk, value head) workspace block
   T* A;        // NTRI fragment-native blocks of A'
   T* MP;       // NTRI fragment-native blocks of MP
-  float* gam;  // [64]
-  float* tail; // [64]
+  float* gk;   // [64] gamma_i * rk_i
+  float* tk;   // [64] exp(G_last - G_i) * rk_i
+  float* gq;   // [64] gamma_i * rq_i
+  float* gl;   // [64] gamma_last (every entry)
   __device__ Block(void* base, size_t gc, int Hv, int h) {
-    char* b = static_cast<char*>(base) + (gc * Hv + h) * (2 * NTRI * FRAG * sizeof(T) + 512);
+    char* b = static_cast<char*>(base) + (gc * Hv + h) * (2 * NTRI * FRAG * sizeof(T) + 1024);
     A = reinterpret_cast<T*>(b);
     MP = A + NTRI * FRAG;
-    gam = reinterpret_cast<float*>(MP + NTRI * FRAG);
-    tail = gam + 64;
+    gk = reinterpret_cast<float*>(MP + NTRI * FRAG);
+    tk = gk + 64;
+    gq = gk + 128;
+    gl = gk + 192;
   }
 };
+
+// Input prologue helpers (fp32).  softplus(x) = log(1 + e^x), returned as x
+// itself above 20 where the two agree to fp32 precision.
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float gate_log_decay(const Prologue& pr, int h, float a) {
+  const float dtb = pr.dt_bias != nullptr ? pr.dt_bias[h] : 0.f;
+  return -expf(pr.A_log[h]) * softplus_f(a + dtb);
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
+// Sum of squares of the 8 values of a fragment (16-bit) or of its two fp32 halves.
+template <typename T>
+__device__ __forceinline__ float frag_sumsq(const Frag<T>& f) {
+  float s = 0.f;
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = fmaf(f.lo[j], f.lo[j], fmaf(f.hi[j], f.hi[j], s));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = Elem<T>::to_f(f.v[j]);
+      s = fmaf(x, x, s);
+    }
+  }
+  return s;
+}
 
 // ---------------------------------------------------------------------------
 // 2. chunk prep: one wave per (chunk, value head), 1-D grid.
@@ -202,8 +232,14 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
   constexpr float LOG2E = 1.4426950408889634f;
   __shared__ __align__(16) float Ld[HPW][4 * 16 * DS];   // diagonal blocks of L, per head
   __shared__ __align__(16) float Xd[4 * 16 * DS];        // their inverses, row-major
-  __shared__ __align__(16) float Gs[HPW][64];            // log2 cumulative decay
+  // log2 cumulative decay G_i log2(e) with the log2 inverse norms folded in:
+  // rows of L (+ log2 rk_i), columns of L and MP (- log2 rk_j), rows of MP
+  // (+ log2 rq_i); all three are G log2(e) without the l2norm prologue
+  __shared__ __align__(16) float GR[HPW][64];
+  __shared__ __align__(16) float GC[HPW][64];
+  __shared__ __align__(16) float GQ[HPW][64];
   __shared__ __align__(16) float Bs[HPW][64];            // beta
+  __shared__ __align__(16) float Rk[64], Rq[64];         // inverse norms of k_i, q_i
 
   // One item = (chunk, HPW value heads that share a key head).  XCD-aware
   // order: workgroup w runs on XCD w % 8; each XCD gets a contiguous run of
@@ -234,13 +270,47 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
       qa[r][kb] = gload_frag<T, DK>(qp + row_off(16 * r + i16), kb, g4);
     }
 
-  // ---- per head: log2 cumulative decay, beta, gamma and tail ---------------
+  // ---- l2norm prologue: inverse norms of the chunk's k and q rows (1 for
+  //      rows past the chunk end), shared by the key head's value heads -------
+  float rk = 1.f, rq = 1.f;
+  if (p.pro.l2norm) {
+    Rk[lane] = 1.f;
+    Rq[lane] = 1.f;
+#pragma unroll
+    for (int r = 0; r < nrt; ++r) {
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sk += frag_sumsq<T>(kf[r][kb]);
+        sq += frag_sumsq<T>(qa[r][kb]);
+      }
+      // the four lanes holding parts of row 16r + i16 are i16 + 16 g
+      sk += __shfl_xor(sk, 16);
+      sk += __shfl_xor(sk, 32);
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      const int row = 16 * r + i16;
+      if (g4 == 0 && row < len) {
+        Rk[row] = 1.f / sqrtf(sk + p.pro.eps);
+        Rq[row] = 1.f / sqrtf(sq + p.pro.eps);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    rk = Rk[lane];
+    rq = Rq[lane];
+  }
+  const float lk = p.pro.l2norm ? log2f(rk) : 0.f, lq = p.pro.l2norm ? log2f(rq) : 0.f;
+
+  // ---- per head: gates, log2 cumulative decay, beta and the block factors ---
 #pragma unroll
   for (int v = 0; v < HPW; ++v) {
     const int h = h0 + v;
     const size_t gi = (size_t)(t0 + min(lane, len - 1)) * p.Hv + h;
-    const float gv = lane < len ? p.g[gi] : 0.f;
-    const float bv = lane < len ? p.beta[gi] : 0.f;
+    float gv = lane < len ? p.g[gi] : 0.f;
+    float bv = lane < len ? p.beta[gi] : 0.f;
+    if (p.pro.A_log != nullptr && lane < len) gv = gate_log_decay(p.pro, h, gv);
+    if (p.pro.beta_logit && lane < len) bv = sigmoid_f(bv);
     float x = gv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -248,11 +318,16 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
       if (lane >= off) x += y;
     }
     const float glast = __shfl(x, C - 1);
-    Gs[v][lane] = x * LOG2E;
+    GR[v][lane] = x * LOG2E + lk;
+    GC[v][lane] = x * LOG2E - lk;
+    GQ[v][lane] = x * LOG2E + lq;
     Bs[v][lane] = bv;
     Block<T> blk(p.chunk_data, (size_t)gc, p.Hv, h);
-    blk.gam[lane] = expf(x);
-    blk.tail[lane] = expf(glast - x);
+    const float gam = expf(x);
+    blk.gk[lane] = gam * rk;
+    blk.tk[lane] = expf(glast - x) * rk;
+    blk.gq[lane] = gam * rq;
+    blk.gl[lane] = expf(glast);
   }
 #pragma unroll
   for (int r = 0; r < nrt; ++r)
@@ -276,11 +351,11 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
     const int i = 16 * r + i16;
 #pragma unroll
     for (int v = 0; v < HPW; ++v) {
-      const float gi = Gs[v][i];
+      const float gi = GQ[v][i];
       f32x4 mp[nrt];
 #pragma unroll
       for (int c = 0; c <= r; ++c) {
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[v][16 * c + 4 * g4]);
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&GC[v][16 * c + 4 * g4]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int j = 16 * c + 4 * g4 + q;
@@ -318,9 +393,9 @@ __global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
       for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kk, kf[r][kb], kf[c][kb]);
 #pragma unroll
       for (int v = 0; v < HPW; ++v) {
-        const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[v][16 * r + 4 * g4]);
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(&GR[v][16 * r + 4 * g4]);
         const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[v][16 * r + 4 * g4]);
-        const float gj = Gs[v][16 * c + i16];
+        const float gj = GC[v][16 * c + i16];
         f32x4 l;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -476,7 +551,7 @@ struct StateSmem {
   static constexpr int KB = 64 * ROWB;              // K (or Q) tile bytes
   static constexpr int VB = 64 * SW * ES;           // V tile bytes (up to SW columns)
   static constexpr int AB = 2 * NTRI * FB;          // A' and MP fragments
-  static constexpr int STAGE = 2 * KB + VB + AB + 512;
+  static constexpr int STAGE = 2 * KB + VB + AB + 1024;
   static constexpr int KTB = NKT * FB;              // K^T fragments
   static constexpr int SXB = NG * NSB * FB;         // state fragments, one set per column group
   static constexpr int DXB = NG * 2 * FB;           // Delta fragments, one set per column group
@@ -610,7 +685,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       const int j = wq + NG * m;
       if (j < NA) dma16(ab + (uint32_t)((j * 64 + lane) * 16), sb + SM::OA + j * 1024);
     }
-    if (wq == NG - 1 && lane < 32) dma16(reinterpret_cast<const char*>(blk.gam) + 16 * lane, sb + SM::OG);
+    if (wq == NG - 1) dma16(reinterpret_cast<const char*>(blk.gk) + 16 * lane, sb + SM::OG);
   };
 
 
@@ -844,7 +919,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
 #pragma unroll
       for (int u = 0; u < NU && u < LA; ++u)
         kt[u] = load_frag_native<T>(KT + ((2 * (u % NST) + u / NST) * 64 + lane) * 8);
-      const float gl = GT[C - 1];
+      const float gl = GT[192];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < NST; ++r)
@@ -884,7 +959,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       f32x4 O[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 128 + 16 * r + 4 * g4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) O[r][q] = gm[q] * QSa[r][q];
         if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 0)) * 64 + lane) * 8), Db0);

@@ -120,6 +120,11 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
   const T* __restrict__ vp = static_cast<const T*>(p.v);
   T* __restrict__ op = static_cast<T*>(p.o);
 
+  // gate prologue constants of this head: g = -exp(A_log) softplus(g_in + dt_bias)
+  const bool gate = p.pro.A_log != nullptr;
+  const float negA = gate ? -expf(p.pro.A_log[h]) : 0.f;
+  const float dtb = gate && p.pro.dt_bias != nullptr ? p.pro.dt_bias[h] : 0.f;
+
   auto load_tok = [&](int t, TokenIn<T, RPL>& in) {
     const size_t qk = ((size_t)t * p.Hq + hk) * DK + row0;
     in.k.load(kp + qk);
@@ -154,7 +159,6 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
   }
   const size_t R = (size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * dv;
   const bool write_key = (h % G == 0) && slice == 0 && cg == 0;
-
   for (int tb = t0; tb < t1; tb += NPF) {
 #pragma unroll
     for (int u = 0; u < NPF; ++u) {
@@ -162,7 +166,13 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
       if (t >= t1) break;
       const TokenIn<T, RPL> in = ring[u];
       if (t + NPF < t1) load_tok(t + NPF, ring[u]);
-      const float a = expf(in.g);
+      float gt = in.g, bt = in.beta;
+      if (gate) {
+        const float x = gt + dtb;
+        gt = negA * (x > 20.f ? x : log1pf(expf(x)));   // softplus
+      }
+      if (p.pro.beta_logit) bt = 1.f / (1.f + expf(-bt));
+      const float a = expf(gt);
       float kr[RPL];
 #pragma unroll
       for (int r = 0; r < RPL; ++r) kr[r] = in.k.get(r);
@@ -179,20 +189,41 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
         w2 = fmaf(S[r].z, qr, w2); w3 = fmaf(S[r].w, qr, w3);
         kq = fmaf(kr[r], qr, kq);
       }
+      // l2norm prologue: squared norms reduced together with the products above;
+      // the unit vectors enter through their factors rk, rq
+      float sk = 0.f, sq = 0.f;
+      if (p.pro.l2norm) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+          const float qr = in.q.get(r);
+          sk = fmaf(kr[r], kr[r], sk);
+          sq = fmaf(qr, qr, sq);
+        }
+        sk = sum_rowgroups(sk);
+        sq = sum_rowgroups(sq);
+      }
       u0 = sum_rowgroups(u0); u1 = sum_rowgroups(u1); u2 = sum_rowgroups(u2); u3 = sum_rowgroups(u3);
       w0 = sum_rowgroups(w0); w1 = sum_rowgroups(w1); w2 = sum_rowgroups(w2); w3 = sum_rowgroups(w3);
       kq = sum_rowgroups(kq);
+      float rk = 1.f;
+      if (p.pro.l2norm) {
+        rk = rsqrtf(sk + p.pro.eps);
+        const float rq = rsqrtf(sq + p.pro.eps);
+        w0 *= rq; w1 *= rq; w2 *= rq; w3 *= rq; kq *= rk * rq;
+      }
       // delta = beta (v - alpha S^T k); o = scale (alpha S^T q + delta (k.q)) = scale S_t^T q
-      const float d0 = in.beta * (in.v.get(0) - a * u0);
-      const float d1 = in.beta * (in.v.get(1) - a * u1);
-      const float d2 = in.beta * (in.v.get(2) - a * u2);
-      const float d3 = in.beta * (in.v.get(3) - a * u3);
+      const float d0 = bt * (in.v.get(0) - a * (rk * u0));
+      const float d1 = bt * (in.v.get(1) - a * (rk * u1));
+      const float d2 = bt * (in.v.get(2) - a * (rk * u2));
+      const float d3 = bt * (in.v.get(3) - a * (rk * u3));
+      // S = alpha S + (rk k) delta^T
+      const float e0 = rk * d0, e1 = rk * d1, e2 = rk * d2, e3 = rk * d3;
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
-        S[r].x = fmaf(kr[r], d0, a * S[r].x);
-        S[r].y = fmaf(kr[r], d1, a * S[r].y);
-        S[r].z = fmaf(kr[r], d2, a * S[r].z);
-        S[r].w = fmaf(kr[r], d3, a * S[r].w);
+        S[r].x = fmaf(kr[r], e0, a * S[r].x);
+        S[r].y = fmaf(kr[r], e1, a * S[r].y);
+        S[r].z = fmaf(kr[r], e2, a * S[r].z);
+        S[r].w = fmaf(kr[r], e3, a * S[r].w);
       }
       if (rg == 0) {
         store4<T>(op + ((size_t)t * p.Hv + h) * dv + col,
@@ -206,7 +237,7 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
         if (write_key) {
           float* kd = rec + p.Hv + (size_t)hk * DK + row0;
 #pragma unroll
-          for (int r = 0; r < RPL; ++r) kd[r] = kr[r];
+          for (int r = 0; r < RPL; ++r) kd[r] = rk * kr[r];
         }
         if (rg == 0) {   // records are only 4-byte aligned in general (R need not be a multiple of 4)
           float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;

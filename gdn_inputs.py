@@ -141,6 +141,36 @@ def random_case(seed: int, lengths, Hq: int, Hv: int, dk: int, dv: int, dtype: s
     return out
 
 
+def raw_case(seed: int, lengths, Hq: int, Hv: int, dk: int, dv: int, dtype: str,
+             state_std: float = 0.02, dense: bool = False):
+    """Inputs in the form the input prologue consumes (raw projections):
+    q, k ~ N(0,1) * U(0.5, 2) per (token, head), not normalised; v ~ N(0,1);
+    ``g`` = gate pre-activation a ~ N(0,1) and ``beta`` = logit b ~ N(0,1), both
+    fp32; A_log = log U(1, 16) and dt_bias ~ N(0, 0.5^2) per value head (fp32).
+    Draw order: q, k, q/k row scales, v, b, a, A_log, dt_bias, initial state."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(lengths))
+    q = rng.standard_normal((T, Hq, dk))
+    k = rng.standard_normal((T, Hq, dk))
+    q = q * rng.uniform(0.5, 2.0, (T, Hq, 1))
+    k = k * rng.uniform(0.5, 2.0, (T, Hq, 1))
+    v = rng.standard_normal((T, Hv, dv))
+    b = rng.standard_normal((T, Hv))
+    a = rng.standard_normal((T, Hv))
+    A_log = np.log(rng.uniform(1.0, 16.0, Hv))
+    dt_bias = rng.standard_normal(Hv) * 0.5
+    s0 = None
+    if state_std > 0.0:
+        s0 = torch.from_numpy(rng.standard_normal((len(lengths), Hv, dk, dv)) * state_std).float()
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return dict(seed=seed, dtype=dtype, Hq=Hq, Hv=Hv, dk=dk, dv=dv, scale=1.0 / math.sqrt(dk),
+                q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype),
+                g=torch.from_numpy(a).float(), beta=torch.from_numpy(b).float(),
+                A_log=torch.from_numpy(A_log).float(), dt_bias=torch.from_numpy(dt_bias).float(), s0=s0,
+                cu_seqlens=None if dense else torch.from_numpy(cu), lengths=list(lengths), T=T,
+                num_seqs=len(lengths))
+
+
 def random_counts(seed: int, rows: int, capacity: int):
     rng = np.random.default_rng(seed)
     return torch.from_numpy(rng.integers(-2, capacity + 3, size=rows).astype(np.int32))

@@ -81,6 +81,35 @@ typedef struct {
   int32_t dtype; /* gdn_dtype of q, k, v, o */
 } gdn_shape;
 
+/*
+ * Optional input prologue, applied inside the kernels of the *_ex entry points
+ * [executorch issue 23097, "Work to cover": reusing a GDN prefill means adapting
+ * its gate and scaling conventions].  The pages give no formulas; these are the
+ * common ones, each switched on separately.  A zeroed struct (or NULL) is the
+ * identity: q, k, g and beta are used as given.
+ *
+ *  qk_l2norm      nonzero: every q_t and k_t (per key head) is replaced by
+ *                 x * (sum_i x_i^2 + qk_l2norm_eps)^(-1/2), computed in fp32
+ *                 from the input-dtype values.  eps = 0 is allowed; an all-zero
+ *                 row then gives non-finite results.
+ *  qk_l2norm_eps  finite, >= 0 (read only when qk_l2norm is set).
+ *  beta_is_logit  nonzero: beta = 1 / (1 + exp(-b)) of the `beta` input.
+ *  gate_A_log     NULL: `g` holds the log decay.  Otherwise fp32 [Hv] on the
+ *                 device, and the log decay of value head h is
+ *                 -exp(gate_A_log[h]) * softplus(g + gate_dt_bias[h]),
+ *                 softplus(x) = log(1 + exp(x)).
+ *  gate_dt_bias   fp32 [Hv] on the device, or NULL (zeros); only with gate_A_log.
+ * Captured records hold the prologue's results: decay = exp of the gated log
+ * decay, key = the normalised fp32 key, delta with the sigmoid beta.
+ */
+typedef struct {
+  int32_t qk_l2norm;
+  float qk_l2norm_eps;
+  int32_t beta_is_logit;
+  const float* gate_A_log;
+  const float* gate_dt_bias;
+} gdn_prologue;
+
 /* Version of this ABI (bumped on any signature change). */
 int32_t gdn_abi_version(void);
 
@@ -147,6 +176,19 @@ gdn_status gdn_prefill_chunked_states(const gdn_shape* shape, const void* q, con
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_prefill_chunked / gdn_prefill_chunked_states with the input prologue:
+ * `prologue` may be NULL (identity) and `chunk_states` may be NULL (no
+ * boundary states; chunk_states_capacity is then ignored).  Same layouts,
+ * results and errors otherwise.
+ */
+gdn_status gdn_prefill_chunked_ex(const gdn_shape* shape, const gdn_prologue* prologue, const void* q,
+                                  const void* k, const void* v, const float* g, const float* beta,
+                                  const float* initial_state, int64_t initial_state_batch_stride,
+                                  const int32_t* cu_seqlens, int32_t chunk_size, void* o,
+                                  float* final_state, float* chunk_states, int64_t chunk_states_capacity,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Recurrent step with compact state-update capture [onnxruntime PR 32767,
  * "Changes": state_update_capacity, the required [batch] capture_count input,
  * the packed float32 state_update output, clamped per-row prefix capture,
@@ -178,6 +220,14 @@ gdn_status gdn_recurrent_step(const gdn_shape* shape, const void* q, const void*
                               const int32_t* cu_seqlens, void* o, float* final_state,
                               int32_t state_update_capacity, const int32_t* capture_count,
                               int32_t state_update_active, float* state_update, void* stream);
+
+/* gdn_recurrent_step with the input prologue (`prologue` may be NULL). */
+gdn_status gdn_recurrent_step_ex(const gdn_shape* shape, const gdn_prologue* prologue, const void* q,
+                                 const void* k, const void* v, const float* g, const float* beta,
+                                 const float* initial_state, int64_t initial_state_batch_stride,
+                                 const int32_t* cu_seqlens, void* o, float* final_state,
+                                 int32_t state_update_capacity, const int32_t* capture_count,
+                                 int32_t state_update_active, float* state_update, void* stream);
 
 /*
  * Replay of captured state updates [onnxruntime PR 32767, "Changes" and

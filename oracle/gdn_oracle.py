@@ -154,6 +154,31 @@ def recurrent(q, k, v, g, beta, scale, Hq, Hv, cu_seqlens=None, num_seqs=None,
     return out
 
 
+def prologue(q, k, g, beta, qk_l2norm=False, eps=1e-6, beta_is_logit=False, A_log=None, dt_bias=None):
+    """The optional input prologue, in fp64: returns (q, k, g, beta) as the
+    recurrence consumes them.
+
+    [executorch issue 23097, "Work to cover"]: reusing a GDN kernel means
+    adapting its gate and scaling conventions; the pages give no formulas, so
+    the common ones are taken, each switched on separately:
+      qk_l2norm:     x / sqrt(sum_i x_i^2 + eps) for every q_t and k_t (last axis)
+      beta_is_logit: beta = 1 / (1 + exp(-b))
+      A_log [Hv]:    g = -exp(A_log[h]) * softplus(g_in + dt_bias[h]),
+                     softplus(x) = log(1 + exp(x)); dt_bias None means 0
+    """
+    q, k, g, beta = (_f64(x) for x in (q, k, g, beta))
+    if qk_l2norm:
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+    if beta_is_logit:
+        beta = 1.0 / (1.0 + np.exp(-beta))
+    if A_log is not None:
+        A = _f64(A_log)
+        dt = np.zeros_like(A) if dt_bias is None else _f64(dt_bias)
+        g = -np.exp(A)[None, :] * np.logaddexp(0.0, g + dt[None, :])   # logaddexp(0, x) = softplus(x)
+    return q, k, g, beta
+
+
 def capture(k, alpha, delta, Hq, Hv, capacity, capture_count, active,
             cu_seqlens=None, num_seqs=None):
     """Expected compact state-update buffer and the mask of specified entries.

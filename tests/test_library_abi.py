@@ -103,13 +103,13 @@ def test_workspace_validation_and_sizing(lib):
     sh = shape()
     need = gdn.gdn_prefill_workspace_bytes(sh, 64, False)
     # dense: ceil(64/64)*B chunks fit in the bound (B*T/C + B + 1) * Hv blocks
-    assert need > 0 and need >= (2 + 2 + 1) * 4 * (2 * 6 * 512 * 2 + 512)
+    assert need > 0 and need >= (2 + 2 + 1) * 4 * (2 * 6 * 512 * 2 + 1024)
     assert gdn.gdn_prefill_workspace_bytes(sh, 48, False) == 0
     assert gdn.gdn_prefill_workspace_bytes(shape(dk=96), 64, False) == 0
     rag = gdn.gdn_prefill_workspace_bytes(shape(B=4, T=14286, Hq=16, Hv=32), 64, True)
     max_chunks = 14286 // 64 + 4 + 1
     head = -(-(32 + max_chunks * 8) // 256) * 256      # offsets (B+1, padded to 16 B) + chunk table
-    assert rag == head + max_chunks * 32 * (2 * 6 * 512 * 2 + 512)
+    assert rag == head + max_chunks * 32 * (2 * 6 * 512 * 2 + 1024)
     assert prefill(lib, sh, ws=NULL, wsb=0) == gdn.GDN_ERR_INVALID_ARG and "workspace" in last(lib)
     assert prefill(lib, sh, ws=ctypes.c_void_p(0x40000008), wsb=need) == gdn.GDN_ERR_INVALID_ARG
 
@@ -131,6 +131,30 @@ def test_chunk_states_validation(lib):
     assert call(FAKE, 4) == gdn.GDN_ERR_INVALID_ARG and "overlaps" in last(lib)
     # a huge capacity is clamped to the chunk bound (no size overflow) and still overlap-checked
     assert call(ctypes.c_void_p(0x40000000 - 1024), 1 << 60) == gdn.GDN_ERR_INVALID_ARG and "workspace" in last(lib)
+
+
+def test_prologue_validation(lib):
+    sh = shape()
+    ws = ctypes.c_void_p(0x40000000)
+    wsb = gdn.gdn_prefill_workspace_bytes(sh, 64, False)
+
+    def pre(pro):
+        return lib.gdn_prefill_chunked_ex(ctypes.byref(sh), ctypes.byref(pro), FAKE, FAKE, FAKE, FAKE, FAKE, NULL,
+                                          0, NULL, 64, ctypes.c_void_p(0x900000), NULL, NULL, 0, ws, wsb, NULL)
+
+    def rec(pro):
+        return lib.gdn_recurrent_step_ex(ctypes.byref(sh), ctypes.byref(pro), FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 0,
+                                         NULL, ctypes.c_void_p(0x900000), NULL, 0, NULL, 1, NULL, NULL)
+    for call in (pre, rec):
+        assert call(gdn.gdn_prologue(1, -1.0, 0, None, None)) == gdn.GDN_ERR_INVALID_ARG and "eps" in last(lib)
+        assert call(gdn.gdn_prologue(1, float("nan"), 0, None, None)) == gdn.GDN_ERR_INVALID_ARG
+        assert call(gdn.gdn_prologue(0, 0.0, 0, None, 0x20000)) == gdn.GDN_ERR_INVALID_ARG and "dt_bias" in last(lib)
+        assert call(gdn.gdn_prologue(0, 0.0, 1, 0x20002, None)) == gdn.GDN_ERR_INVALID_ARG and "aligned" in last(lib)
+        # a valid prologue still fails on the (invalid) shape before anything is enqueued
+    bad = gdn.gdn_shape(2, 64, 2, 5, 128, 128, 0.088, gdn.GDN_BF16)
+    ok = gdn.gdn_prologue(1, 1e-6, 1, 0x20000, 0x20010)
+    assert lib.gdn_recurrent_step_ex(ctypes.byref(bad), ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL,
+                                     ctypes.c_void_p(0x900000), NULL, 0, NULL, 1, NULL, NULL) == gdn.GDN_ERR_INVALID_ARG
 
 
 def test_replay_and_snapshot_validation(lib):

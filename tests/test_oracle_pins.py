@@ -267,6 +267,47 @@ def test_chunk_boundary_states():
     np.testing.assert_allclose(r["boundary"][1], p["final"][0], atol=1e-14)
 
 
+def test_prologue_closed_forms():
+    """Input prologue pins: a 3-4-5 key normalises to (0.6, 0.8); sigmoid(0) =
+    1/2 and sigmoid(ln 3) = 3/4; with A_log = 0 the gate's decay is
+    exp(-softplus(x)) = 1 / (1 + e^x), and with A_log = ln 2 its square; the
+    identity prologue returns its inputs."""
+    q = np.array([[[0.0, 2.0]]])
+    k = np.array([[[3.0, 4.0]]])
+    a = np.array([[0.3, -1.2, 2.5]])
+    b = np.array([[0.0, np.log(3.0), -np.log(3.0)]])
+    qn, kn, g, beta = oracle.prologue(q, k, a, b, qk_l2norm=True, eps=0.0, beta_is_logit=True,
+                                      A_log=np.zeros(3), dt_bias=np.array([0.1, 0.0, -0.5]))
+    np.testing.assert_allclose(kn[0, 0], [0.6, 0.8], rtol=1e-15)
+    np.testing.assert_allclose(qn[0, 0], [0.0, 1.0], rtol=1e-15)
+    np.testing.assert_allclose(beta[0], [0.5, 0.75, 0.25], rtol=1e-15)
+    x = a[0] + np.array([0.1, 0.0, -0.5])
+    np.testing.assert_allclose(np.exp(g[0]), 1.0 / (1.0 + np.exp(x)), rtol=1e-14)
+    _, _, g2, _ = oracle.prologue(q, k, a, b, A_log=np.full(3, np.log(2.0)))
+    np.testing.assert_allclose(np.exp(g2[0]), (1.0 + np.exp(a[0])) ** -2, rtol=1e-14)
+    # eps enters under the root
+    _, ke, _, _ = oracle.prologue(q, k, a, b, qk_l2norm=True, eps=11.0)
+    np.testing.assert_allclose(ke[0, 0], [0.5, 4.0 / 6.0], rtol=1e-15)
+    for x0, x1 in zip((q, k, a, b), oracle.prologue(q, k, a, b)):
+        np.testing.assert_array_equal(x0, x1)
+
+
+def test_prologue_l2norm_scale_invariance():
+    """With the l2norm prologue (eps = 0) the layer output does not change when
+    each q_t and k_t is scaled by its own positive factor, and equals the plain
+    recurrence on unit-norm inputs."""
+    rng = np.random.default_rng(25)
+    T, Hq, Hv, dk, dv = 9, 2, 4, 5, 3
+    q, k, v, g, beta = _case(rng, T, Hq, Hv, dk, dv)
+    cq = rng.uniform(0.2, 5.0, (T, Hq, 1))
+    ck = rng.uniform(0.2, 5.0, (T, Hq, 1))
+    p1 = oracle.prologue(q * cq, k * ck, g, beta, qk_l2norm=True, eps=0.0)
+    r1 = oracle.recurrent(p1[0], p1[1], v, p1[2], p1[3], 0.7, Hq, Hv)
+    r0 = oracle.recurrent(q, k, v, g, beta, 0.7, Hq, Hv)          # _case draws unit-norm q, k
+    np.testing.assert_allclose(r1["o"], r0["o"], atol=1e-13)
+    np.testing.assert_allclose(r1["final"], r0["final"], atol=1e-13)
+
+
 def test_shared_key_heads_equal_single_head_runs():
     rng = np.random.default_rng(23)
     T, Hq, Hv, dk, dv = 11, 2, 6, 5, 4
