@@ -18,8 +18,12 @@ Timing: torch.cuda events around K timed steps (our kernels run on torch's
 current stream) give ms_per_step and value.  A second pass over K more steps,
 with every launch bracketed by the library's own HIP-event pairs on the launch
 stream, gives the per-kernel durations (roofline, breakdown); those event pairs
-cost ~2-3 us per launch boundary, so they are kept off the first pass.  Prints
-ONE JSON line.
+cost ~2-3 us per launch boundary, so they are kept off the first pass.
+
+The breakdown also times, outside the step, the prefix-reuse batch: 16 rows x
+256 bf16 tokens continuing from one broadcast snapshot of a 4096-token prefix
+(event-timed loop over two distinct resident batches), without and with the
+rows' final states.  Prints ONE JSON line.
 """
 
 from __future__ import annotations
@@ -156,6 +160,57 @@ def cpu_baseline(pre, dec, budget_s):
 
 
 # ----------------------------------------------------------------------------- #
+def _prefix_batch(gdn, gi, dev, C, iters):
+    """Per-call time of the prefix-reuse batch prefill (event-timed loop over two
+    distinct resident batches), its MFMA fraction, and per-kernel durations."""
+    import torch
+    pre = gi.make("prefix_reuse", part="prefix")
+    Hq, Hv, dk, dv = pre["Hq"], pre["Hv"], pre["dk"], pre["dv"]
+    p = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in pre.items()}
+    _, pfin = gdn.gdn_prefill_chunked(*[p[x][None] for x in ("q", "k", "v", "g", "beta")], scale=pre["scale"],
+                                      chunk_size=C)
+    snap = gdn.gdn_state_snapshot(pfin)
+    bts = []
+    for bi in range(2):
+        bt = gi.make("prefix_reuse", part="batch", batch_index=bi)
+        B = bt["num_seqs"]
+        bts.append([bt[x].to(dev).reshape(B, -1, *bt[x].shape[1:]) for x in ("q", "k", "v", "g", "beta")])
+    B, L = bt["num_seqs"], bt["lengths"][0]
+    o = torch.empty_like(bts[0][2])
+    fin = torch.empty((B, Hv, dk, dv), device=dev)
+    sh = gdn.gdn_shape(B, L, Hq, Hv, dk, dv, bt["scale"], gdn.GDN_BF16)
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(sh, C, False), dtype=torch.uint8, device=dev)
+    F = prefill_flops([L] * B, C, Hq, Hv, dk, dv)
+    res = {"workload": f"{B} rows x {L} tokens from one broadcast snapshot of a {pre['T']}-token prefix",
+           "algorithmic_gflop": F / 1e9}
+    for name, finals in (("no_finals", None), ("with_finals", fin)):
+        def call(i):
+            gdn.gdn_prefill_chunked(*bts[i % 2], scale=bt["scale"], initial_state=snap,
+                                    initial_state_batch_stride=0, chunk_size=C, o=o, final_state=finals,
+                                    output_final_state=finals is not None, workspace=ws)
+        for i in range(3):
+            call(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(iters):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / iters
+        res[name] = {"us": us, "tokens_per_s": B * L / (us * 1e-6), "tflops": F / (us * 1e-6) / 1e12,
+                     "mfma_frac": F / (us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS}
+    gdn.gdn_profile_collect()
+    gdn.gdn_profile_enable(True)
+    for i in range(iters):
+        gdn.gdn_prefill_chunked(*bts[i % 2], scale=bt["scale"], initial_state=snap, initial_state_batch_stride=0,
+                                chunk_size=C, o=o, final_state=None, output_final_state=False, workspace=ws)
+    torch.cuda.synchronize()
+    gdn.gdn_profile_enable(False)
+    res["kernels_no_finals"] = {k: {"avg_us": 1000.0 * ms / n} for k, (n, ms) in gdn.gdn_profile_collect().items()}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -243,6 +298,11 @@ def main():
     prof = gdn.gdn_profile_collect()
     ms_step_profiled = ep0.elapsed_time(ep1) / args.steps
 
+    # Timed region 3 (reported in the breakdown only): the prefix-reuse batch,
+    # 16 rows x 256 tokens continuing from one broadcast snapshot of a
+    # 4096-token prefix, without and with the rows' final states.
+    batch = _prefix_batch(gdn, gi, dev, C, args.steps)
+
     kernels = {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in prof.items()}
     per_step_us = {k: 1000.0 * ms / args.steps for k, (n, ms) in prof.items()}
 
@@ -269,6 +329,7 @@ def main():
                    "gbs": rbytes / (t_rep_us * 1e-6) / 1e9,
                    "hbm_frac": rbytes / (t_rep_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
         "snapshot": {"us": t_snap_us, "gbs": 2 * N * Hv * dk * dv * 4 / (t_snap_us * 1e-6) / 1e9},
+        "prefix_batch": batch,
     }
 
     # dominant kernel: the one with the largest time per step

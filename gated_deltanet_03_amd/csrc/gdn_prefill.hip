@@ -226,7 +226,7 @@ __device__ __forceinline__ void mma_tn(f32x4& acc, const f32x4& e, const f32x4& 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T, int DK, int C, int HPW>
-__global__ __launch_bounds__(64, 3) void chunk_prep_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int nrt = C / 16;
   constexpr int NKB = DK >= 32 ? DK / 32 : 1;
   constexpr float LOG2E = 1.4426950408889634f;
@@ -537,6 +537,26 @@ __device__ __forceinline__ int perm_dk(int r) {
   }
 }
 
+// Row-dependent XOR swizzle of the 16-byte pieces of a K/Q tile row: piece p of
+// row r is stored at slot p ^ kq_swz(r).  Any bijection of r mod 16 keeps the
+// fragment reads (16 consecutive rows, one piece each) on distinct banks; for
+// 16-piece rows read by transpose reads (TR) the two 2-bit halves of r are swapped so that the transpose
+// reads of K^T fragments (4 rows x 4 pieces per 16 lanes) also hit 16
+// distinct pieces.
+template <int PPR, bool TR>
+__device__ __forceinline__ int kq_swz(int r) {
+  if constexpr (TR && PPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return r % PPR;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte chunks addressed by lanes
+// 4j + i / 4, j = 0..3 (its element j).
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
 template <typename T, int DK, int NG>
 struct StateSmem {
   static constexpr int ES = (int)sizeof(T);
@@ -567,6 +587,10 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   using SM = StateSmem<T, DK, NG>;
   constexpr int SW = SM::SW;
   constexpr int nrt = C / 16;
+  // K^T fragments by transpose reads of the K tile (16-bit, dk = 128, both
+  // 16-token tiles of each 32-token block present); else built by the output
+  // waves with permutation products
+  constexpr bool TRK = sizeof(T) == 2 && DK == 128 && C >= 32;
   constexpr int NST = SM::NST, NSB = SM::NSB, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
   constexpr int RPI_K = 64 / PPR;         // K rows per DMA instruction
   constexpr int NA = SM::AB / 1024;       // DMA instructions for A' and MP
@@ -627,7 +651,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   for (int m = 0; m < KPW; ++m) {
     const int j = wq + NG * m;
     const int r = RPI_K * j + lane / PPR;
-    const int pp = (lane % PPR) ^ (r % PPR);           // logical piece stored at this slot
+    const int pp = (lane % PPR) ^ kq_swz<PPR, TRK>(r);      // logical piece stored at this slot
     krow[m] = r;
     kvo[m] = (uint32_t)(((r * p.Hq + hk) * DK + pp * PER) * ES);
   }
@@ -695,16 +719,16 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     if constexpr (DK >= 32) {
       const int piece = (32 * kb + 8 * g4) * ES / 16;
       if constexpr (ES == 2) {
-        return load_frag_8<T>(reinterpret_cast<const T*>(tile + r * SM::ROWB + ((piece ^ (r % PPR)) << 4)));
+        return load_frag_8<T>(reinterpret_cast<const T*>(tile + r * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r)) << 4)));
       } else {
         // fp32: 8 elements span two pieces
-        const T* a = reinterpret_cast<const T*>(tile + r * SM::ROWB + ((piece ^ (r % PPR)) << 4));
-        const T* b = reinterpret_cast<const T*>(tile + r * SM::ROWB + (((piece + 1) ^ (r % PPR)) << 4));
+        const T* a = reinterpret_cast<const T*>(tile + r * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r)) << 4));
+        const T* b = reinterpret_cast<const T*>(tile + r * SM::ROWB + (((piece + 1) ^ kq_swz<PPR, TRK>(r)) << 4));
         return load_frag_rows<T>(a, b);
       }
     } else {
       const int b = 4 * g4 * ES;
-      const T* a = reinterpret_cast<const T*>(tile + r * SM::ROWB + ((((b >> 4) ^ (r % PPR))) << 4) + (b & 15));
+      const T* a = reinterpret_cast<const T*>(tile + r * SM::ROWB + ((((b >> 4) ^ kq_swz<PPR, TRK>(r))) << 4) + (b & 15));
       Frag<T> f = load_frag_rows<T>(a, a);
       if constexpr (ES == 2) {
 #pragma unroll
@@ -882,7 +906,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       //      16 tokens later (hi): tiles D(2kb, rt), D(2kb+1, rt) of K * P, P the
       //      0/1 matrix picking dk column perm_dk(16rt + n) -------------------------
 #pragma unroll
-      for (int f0 = 0; f0 < SM::NKT; f0 += NG) {
+      for (int f0 = 0; f0 < (TRK ? 0 : SM::NKT); f0 += NG) {
         const int f = f0 + wq;
         if (f < SM::NKT) {
           const int rt = f >> 1, kb = f & 1;
@@ -913,12 +937,30 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     lds_barrier();   // MID: Delta and K^T fragments are in LDS; state fragments consumed
     if (chain) {
       // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
-      // K^T fragments read eight ahead of the products that use them
-      constexpr int NKB2 = nrt > 2 ? 2 : 1, NU = NKB2 * NST, LA = 8;
+      // K^T fragment (state tile rt, token block kb): for state row 16rt + n,
+      // K[32kb + 4g + j][dk(16rt + n)] in slots j < 4 and the same 16 tokens
+      // later in slots 4..7.  With transpose reads, lane s of each 16-lane group
+      // addresses row 32kb + 4g + s/4 (+16), dk columns 32(rt/2) + 8(s%4) +
+      // 4(rt%2) .. +3 of the K tile, whose column block is perm_dk's.
+      auto kt_frag = [&](int rt, int kb) {
+        if constexpr (TRK) {
+          const int piece = 4 * (rt >> 1) + (i16 & 3);
+          const int r0 = 32 * kb + 4 * g4 + (i16 >> 2), r1 = r0 + 16;
+          const s16x4 a = lds_read_tr16(Kt + r0 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r0)) << 4) + 8 * (rt & 1));
+          const s16x4 b = lds_read_tr16(Kt + r1 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r1)) << 4) + 8 * (rt & 1));
+          const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+          Frag<T> f;
+          f.v = __builtin_bit_cast(decltype(f.v), make_uint4(ua.x, ua.y, ub.x, ub.y));
+          return f;
+        } else {
+          return load_frag_native<T>(KT + ((2 * rt + kb) * 64 + lane) * 8);
+        }
+      };
+      // K^T fragments read LA ahead of the products that use them
+      constexpr int NKB2 = nrt > 2 ? 2 : 1, NU = NKB2 * NST, LA = TRK ? 7 : 8;
       Frag<T> kt[NU];
 #pragma unroll
-      for (int u = 0; u < NU && u < LA; ++u)
-        kt[u] = load_frag_native<T>(KT + ((2 * (u % NST) + u / NST) * 64 + lane) * 8);
+      for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
       const float gl = GT[192];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -929,7 +971,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       for (int u = 0; u < NU; ++u) {
         mma<T>(S[u % NST], kt[u], u / NST == 0 ? Tb0 : Tb1);
         __builtin_amdgcn_sched_barrier(0);
-        if (u + LA < NU) kt[u + LA] = load_frag_native<T>(KT + ((2 * ((u + LA) % NST) + (u + LA) / NST) * 64 + lane) * 8);
+        if (u + LA < NU) kt[u + LA] = kt_frag((u + LA) % NST, (u + LA) / NST);
         __builtin_amdgcn_sched_barrier(0);
       }
       // next chunk's state fragments (kept for the chain's K*S, stored for the output wave)
