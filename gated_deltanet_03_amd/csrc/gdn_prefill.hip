@@ -810,6 +810,30 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     const float* GT = reinterpret_cast<const float*>(sb + SM::OG);
     f32x4 QSa[4];
     Frag<T> Tb0, Tb1;
+    // K^T fragment (state tile rt, token block kb): for state row 16rt + n,
+    // K[32kb + 4g + j][dk(16rt + n)] in slots j < 4 and the same 16 tokens later
+    // in slots 4..7.  With transpose reads, lane s of each 16-lane group
+    // addresses row 32kb + 4g + s/4 (+16), dk columns 32(rt/2) + 8(s%4) +
+    // 4(rt%2) .. +3 of the K tile, whose column block is perm_dk's.
+    auto kt_frag = [&](int rt, int kb) {
+      if constexpr (TRK) {
+        const int piece = 4 * (rt >> 1) + (i16 & 3);
+        const int r0 = 32 * kb + 4 * g4 + (i16 >> 2), r1 = r0 + 16;
+        const s16x4 a = lds_read_tr16(Kt + r0 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r0)) << 4) + 8 * (rt & 1));
+        const s16x4 b = lds_read_tr16(Kt + r1 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r1)) << 4) + 8 * (rt & 1));
+        const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+        Frag<T> f;
+        f.v = __builtin_bit_cast(decltype(f.v), make_uint4(ua.x, ua.y, ub.x, ub.y));
+        return f;
+      } else {
+        return load_frag_native<T>(KT + ((2 * rt + kb) * 64 + lane) * 8);
+      }
+    };
+    // K^T fragments are read LA ahead of the state-update products that use
+    // them; with transpose reads the first LA are issued before MID
+    constexpr int NKB2 = nrt > 2 ? 2 : 1, NU = NKB2 * NST, LA = TRK ? 7 : 8;
+    Frag<T> kt[NU];
+    float gl = 0.f;
     if (chain) {
       // ---- LDS reads and products in a fixed interleave: at most ~14 reads in
       //      flight (the LDS counter a wait can name stops at 15), K blocks two
@@ -876,6 +900,13 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       }
 #pragma unroll
       for (int r = 2; r < nrt; ++r) mma<T>(D[r], aa[tri_idx(r, 1)], Xb1);
+      if constexpr (TRK) {   // the K tile is complete since TOP: K^T reads overlap Delta's exchange
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
+        gl = GT[192];
+        __builtin_amdgcn_sched_barrier(0);
+      }
       store_frag_native<T>(dx_mine, make_frag<T>(D[0], D[1]));
       store_frag_native<T>(dx_mine + 512, make_frag<T>(D[2], D[3]));
       // ---- tail-weighted Delta for the state update ---------------------------
@@ -937,49 +968,38 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     lds_barrier();   // MID: Delta and K^T fragments are in LDS; state fragments consumed
     if (chain) {
       // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
-      // K^T fragment (state tile rt, token block kb): for state row 16rt + n,
-      // K[32kb + 4g + j][dk(16rt + n)] in slots j < 4 and the same 16 tokens
-      // later in slots 4..7.  With transpose reads, lane s of each 16-lane group
-      // addresses row 32kb + 4g + s/4 (+16), dk columns 32(rt/2) + 8(s%4) +
-      // 4(rt%2) .. +3 of the K tile, whose column block is perm_dk's.
-      auto kt_frag = [&](int rt, int kb) {
-        if constexpr (TRK) {
-          const int piece = 4 * (rt >> 1) + (i16 & 3);
-          const int r0 = 32 * kb + 4 * g4 + (i16 >> 2), r1 = r0 + 16;
-          const s16x4 a = lds_read_tr16(Kt + r0 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r0)) << 4) + 8 * (rt & 1));
-          const s16x4 b = lds_read_tr16(Kt + r1 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r1)) << 4) + 8 * (rt & 1));
-          const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
-          Frag<T> f;
-          f.v = __builtin_bit_cast(decltype(f.v), make_uint4(ua.x, ua.y, ub.x, ub.y));
-          return f;
-        } else {
-          return load_frag_native<T>(KT + ((2 * rt + kb) * 64 + lane) * 8);
+      if constexpr (!TRK) {   // K^T fragments built by the output waves before MID
+#pragma unroll
+        for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
+        gl = GT[192];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Each tile is scaled by gamma_last right before its first product, and the
+      // next chunk's state fragments of a tile pair (kept for the chain's K*S,
+      // stored for the output wave) are formed two products after the pair's
+      // last one, so VALU work overlaps the matrix products.
+      constexpr int U0 = (NKB2 - 1) * NST;   // first product of the last token block
+      auto next_sb = [&](int rt) {
+        if (rt >= 0 && (rt % 2 == 1 || rt == NST - 1)) {
+          const int kb = rt / 2;
+          Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
+          store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
         }
       };
-      // K^T fragments read LA ahead of the products that use them
-      constexpr int NKB2 = nrt > 2 ? 2 : 1, NU = NKB2 * NST, LA = TRK ? 7 : 8;
-      Frag<T> kt[NU];
-#pragma unroll
-      for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
-      const float gl = GT[192];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int r = 0; r < NST; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) S[r][q] *= gl;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
+        if (u < NST) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) S[u][q] *= gl;
+        }
         mma<T>(S[u % NST], kt[u], u / NST == 0 ? Tb0 : Tb1);
         __builtin_amdgcn_sched_barrier(0);
         if (u + LA < NU) kt[u + LA] = kt_frag((u + LA) % NST, (u + LA) / NST);
+        if (u - 2 >= U0) next_sb(u - 2 - U0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // next chunk's state fragments (kept for the chain's K*S, stored for the output wave)
-#pragma unroll
-      for (int kb = 0; kb < NSB; ++kb) {
-        Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
-        store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
-      }
+      next_sb(NST - 2);
+      next_sb(NST - 1);
       if constexpr (EMIT) {
         // the state after this chunk's last token, in the [dk, dv] state layout:
         // a wave-uniform row base per store plus one per-lane 32-bit offset
