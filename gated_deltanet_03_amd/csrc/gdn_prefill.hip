@@ -557,7 +557,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
-template <typename T, int DK, int NG>
+// LDS plan of the state kernel.  TR: K^T comes from transpose reads, so no K^T
+// region.
+template <typename T, int DK, int NG, bool TR>
 struct StateSmem {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int SW = 16 * NG;                // columns per workgroup (NG groups of 16)
@@ -572,7 +574,7 @@ struct StateSmem {
   static constexpr int VB = 64 * SW * ES;           // V tile bytes (up to SW columns)
   static constexpr int AB = 2 * NTRI * FB;          // A' and MP fragments
   static constexpr int STAGE = 2 * KB + VB + AB + 1024;
-  static constexpr int KTB = NKT * FB;              // K^T fragments
+  static constexpr int KTB = TR ? 0 : NKT * FB;     // K^T fragments
   static constexpr int SXB = NG * NSB * FB;         // state fragments, one set per column group
   static constexpr int DXB = NG * 2 * FB;           // Delta fragments, one set per column group
   static constexpr int FIXED = KTB + SXB + DXB;
@@ -584,13 +586,13 @@ struct StateSmem {
 
 template <typename T, int DK, int C, int NG, int NDW, bool EMIT>
 __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(PrefillArgs p) {
-  using SM = StateSmem<T, DK, NG>;
-  constexpr int SW = SM::SW;
-  constexpr int nrt = C / 16;
   // K^T fragments by transpose reads of the K tile (16-bit, dk = 128, both
   // 16-token tiles of each 32-token block present); else built by the output
   // waves with permutation products
   constexpr bool TRK = sizeof(T) == 2 && DK == 128 && C >= 32;
+  using SM = StateSmem<T, DK, NG, TRK>;
+  constexpr int SW = SM::SW;
+  constexpr int nrt = C / 16;
   constexpr int NST = SM::NST, NSB = SM::NSB, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
   constexpr int RPI_K = 64 / PPR;         // K rows per DMA instruction
   constexpr int NA = SM::AB / 1024;       // DMA instructions for A' and MP
@@ -1079,7 +1081,7 @@ static int device_cus() {
 
 template <typename T, int DK, int C, int NG, int NDW, bool EMIT>
 static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
-  using SM = StateSmem<T, DK, NG>;
+  using SM = StateSmem<T, DK, NG, sizeof(T) == 2 && DK == 128 && C >= 32>;
   const size_t sm2 = SM::total;
   if (sm2 > 160 * 1024) return hipErrorInvalidValue;
   static bool attr = false;
@@ -1121,10 +1123,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
     prof_end(K_PREP, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // Column groups per workgroup: 2 (32 columns, 4 waves) spreads each head over
-  // more CUs and halves the LDS and load traffic per CU per chunk, which
-  // shortens the sequential chunk step; 4 (64 columns, 8 waves) is kept for
-  // batches with more (sequence, head, slice) work than two workgroups per CU.
+  // Geometry.  While there are at most two (sequence, head, 32-column slice)
+  // items per CU the pass is latency bound: 32-column workgroups (2 chain + 2
+  // output + 2 load-issuing waves) spread each head over more CUs and keep load
+  // issue off the chain.  Beyond that, 64-column workgroups (4 chain + 4 output
+  // waves, the chain issuing the loads), one per CU.  (32-column workgroups of 4
+  // waves with a single stage buffer, two per CU, measured 78 us against 45 us
+  // on the 16 x 256-token batch: each workgroup then waits for its loads.)
   // The chunk-boundary state stores live in a separate instantiation so that
   // the plain prefill keeps its register allocation.
   const bool emit = a.chunk_states != nullptr;

@@ -161,3 +161,26 @@ def test_prefix_snapshot_reuse(gdn):
             ref = oracle_run(bt, heads=heads, s0=pref["final"][:1], broadcast=True)
             for h in heads:
                 assert_close(o[:, h], ref["o"][:, h], "bf16", f"batch {bi} head {h}")
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f16", 32)])
+def test_prefill_many_rows_geometry(gdn, dtype, C):
+    """More (row, head, 32-column slice) items than two per CU (40 x 4 x 4 = 640
+    > 512) selects the 64-column workgroup geometry; ragged rows, random initial
+    states, boundary states included."""
+    rng_lengths = [97, 64, 1, 130, 33] * 8
+    case = gi.random_case(9600 + C, rng_lengths, Hq=2, Hv=4, dk=128, dv=128, dtype=dtype)
+    say(f"case many-rows geometry {dtype} C={C} rows={len(rng_lengths)}")
+    d = to_dev(case)
+    o, fin, cs = gdn.gdn_prefill_chunked_states(*[d[x] for x in ("q", "k", "v", "g", "beta")], scale=case["scale"],
+                                                cu_seqlens=d["cu_seqlens"], chunk_size=C, initial_state=d["s0"])
+    torch.cuda.synchronize()
+    ref = oracle.recurrent(case["q"], case["k"], case["v"], case["g"], case["beta"], case["scale"], 2, 4,
+                           cu_seqlens=case["cu_seqlens"], initial_state=case["s0"], boundary_every=C)
+    assert_close(o, ref["o"], dtype, "o")
+    assert_close(fin, ref["final"], dtype, "final")
+    assert_close(cs, ref["boundary"], dtype, "chunk states")
+    o2, fin2 = gdn.gdn_prefill_chunked(*[d[x] for x in ("q", "k", "v", "g", "beta")], scale=case["scale"],
+                                       cu_seqlens=d["cu_seqlens"], chunk_size=C, initial_state=d["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(fin, fin2)
