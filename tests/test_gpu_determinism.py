@@ -1,0 +1,70 @@
+"""Determinism and geometry independence of the HIP path.
+
+No kernel uses atomics or order-dependent reductions, so repeated calls must be
+bit-identical.  The state pass picks its workgroup geometry from the amount of
+work (32-column workgroups with load-issuing waves while there are at most two
+(sequence, head, 32-column slice) items per CU, 64-column workgroups beyond);
+each 16-column group runs the same instruction sequence in both, so rows must
+give bit-identical results whichever geometry their batch selects.  A race on a
+shared LDS buffer, or indexing that depends on the geometry, breaks these.
+"""
+
+import pytest
+import torch
+
+import gdn_inputs as gi
+from gpu_common import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_03_amd as m
+    m.load_library()
+    return m
+
+
+def run(gdn, d, scale, C, **kw):
+    o, fin = gdn.gdn_prefill_chunked(*[d[x] for x in ("q", "k", "v", "g", "beta")], scale=scale,
+                                     cu_seqlens=d["cu_seqlens"], chunk_size=C, initial_state=d["s0"], **kw)
+    torch.cuda.synchronize()
+    return o, fin
+
+
+def test_repeated_calls_are_bitwise_identical(gdn):
+    case = gi.make("long_varlen")
+    say(f"case determinism long_varlen lengths={case['lengths']}")
+    d = to_dev(case)
+    o1, f1 = run(gdn, d, case["scale"], 64)
+    o2, f2 = run(gdn, d, case["scale"], 64)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    dec = to_dev(gi.make("spec_decode"))
+    args = [dec[x] for x in ("q", "k", "v", "g", "beta")]
+    kw = dict(scale=dec["scale"], initial_state=dec["s0"], cu_seqlens=dec["cu_seqlens"], state_update_capacity=7,
+              capture_count=dec["capture_count"], state_update_active=1)
+    a = gdn.gdn_recurrent_step(*args, **kw)
+    b = gdn.gdn_recurrent_step(*args, **kw)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rows_do_not_depend_on_the_geometry(gdn, dtype):
+    lengths = [150, 64, 3, 97]
+    Hq, Hv = 2, 4
+    case = gi.random_case(9700, lengths, Hq=Hq, Hv=Hv, dk=128, dv=128, dtype=dtype)
+    # 4 rows x 4 heads x 4 slices = 64 items: the 32-column geometry; 40 extra
+    # rows make 704 items > 2 per CU: the 64-column geometry
+    filler = gi.random_case(9701, [80] * 40, Hq=Hq, Hv=Hv, dk=128, dv=128, dtype=dtype)
+    say(f"case geometry independence {dtype} lengths={lengths} + 40 x 80")
+    small = to_dev(case)
+    big = to_dev({k: (torch.cat([case[k], filler[k]]) if k in ("q", "k", "v", "g", "beta", "s0") else case[k])
+                  for k in case})
+    cu = torch.tensor([0] + list(torch.cumsum(torch.tensor(lengths + [80] * 40), 0)), dtype=torch.int32)
+    big["cu_seqlens"] = cu.to(small["q"].device)
+    o1, f1 = run(gdn, small, case["scale"], 64)
+    o2, f2 = run(gdn, big, case["scale"], 64)
+    T = sum(lengths)
+    assert torch.equal(o1, o2[:T]), "outputs differ between the two geometries"
+    assert torch.equal(f1, f2[:len(lengths)]), "final states differ between the two geometries"
