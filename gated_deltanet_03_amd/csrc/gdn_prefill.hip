@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) voi
   constexpr int nrt = C / 16;
   constexpr int NKB = DK >= 32 ? DK / 32 : 1;
   constexpr float LOG2E = 1.4426950408889634f;
-  __shared__ __align__(16) float Ld[HPW][4 * 16 * DS];   // diagonal blocks of L, per head
+  __shared__ __align__(16) float Ld[4 * 16 * DS];        // diagonal blocks of L, one head at a time
   __shared__ __align__(16) float Xd[4 * 16 * DS];        // their inverses, row-major
   // log2 cumulative decay G_i log2(e) with the log2 inverse norms folded in:
   // rows of L (+ log2 rk_i), columns of L and MP (- log2 rk_j), rows of MP
@@ -382,8 +382,12 @@ __global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) voi
   }
 
   // ---- L_ij = beta_i exp(G_i - G_j) (K K^T)_ij, j < i, for every head:
-  //      off-diagonal tiles stay in registers, diagonal tiles go to LDS --------
+  //      off-diagonal tiles stay in registers; the diagonal K K^T tiles are kept
+  //      and scaled into LDS per head just before that head's inverse (one LDS
+  //      buffer for all heads keeps the wave's LDS small enough for three waves
+  //      per SIMD) ---------------------------------------------------------------
   f32x4 Lt[HPW][nrt][nrt];   // [v][r][c], c < r used
+  f32x4 kkd[nrt];            // diagonal tiles of K K^T
 #pragma unroll
   for (int r = 0; r < nrt; ++r) {
 #pragma unroll
@@ -391,6 +395,10 @@ __global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) voi
       f32x4 kk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) gram_mma<T, DK>(kk, kf[r][kb], kf[c][kb]);
+      if (c == r) {
+        kkd[r] = kk;
+        continue;
+      }
 #pragma unroll
       for (int v = 0; v < HPW; ++v) {
         const f32x4 gi = *reinterpret_cast<const f32x4*>(&GR[v][16 * r + 4 * g4]);
@@ -398,27 +406,33 @@ __global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) voi
         const float gj = GC[v][16 * c + i16];
         f32x4 l;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bool below = c < r || i16 < 4 * g4 + q;
-          l[q] = below ? bi[q] * fast_exp2(gi[q] - gj) * kk[q] : 0.f;
-        }
-        if (c < r) {
-          Lt[v][r][c] = l;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) Ld[v][(r * 16 + 4 * g4 + q) * DS + i16] = l[q];
-        }
+        for (int q = 0; q < 4; ++q) l[q] = bi[q] * fast_exp2(gi[q] - gj) * kk[q];
+        Lt[v][r][c] = l;
       }
     }
   }
 
 #pragma unroll
   for (int v = 0; v < HPW; ++v) {
+    // ---- this head's diagonal blocks of L into LDS (strictly lower part) ------
+#pragma unroll
+    for (int r = 0; r < nrt; ++r) {
+      const f32x4 gi = *reinterpret_cast<const f32x4*>(&GR[v][16 * r + 4 * g4]);
+      const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[v][16 * r + 4 * g4]);
+      const float gj = GC[v][16 * r + i16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool below = i16 < 4 * g4 + q;
+        Ld[(r * 16 + 4 * g4 + q) * DS + i16] = below ? bi[q] * fast_exp2(gi[q] - gj) * kkd[r][q] : 0.f;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): every lane's entries are in LDS
+    __builtin_amdgcn_wave_barrier();
     // ---- diagonal blocks: lane (b, r) computes row r of (I + L_bb)^-1 by
     //      back-substitution, X (I + L) = I, over k = 15 .. 1 -----------------
     {
       const int b = lane >> 4, r = lane & 15;
-      const float* Lb = Ld[v] + b * 16 * DS;
+      const float* Lb = Ld + b * 16 * DS;
       float x[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) x[j] = (j == r) ? 1.f : 0.f;
