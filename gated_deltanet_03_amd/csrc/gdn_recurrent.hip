@@ -21,6 +21,8 @@
 // so they run on one XCD and the two 64-byte halves of every 128-byte state
 // line are fetched once into its L2.  The state is read once and written once
 // per call.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -159,6 +161,9 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
   }
   const size_t R = (size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * dv;
   const bool write_key = (h % G == 0) && slice == 0 && cg == 0;
+  // 16-byte record stores: the buffer is 16-byte aligned, Hv and R are
+  // multiples of 4, and a lane's key rows come in fours
+  const bool vec_rec = RPL % 4 == 0 && (reinterpret_cast<uintptr_t>(p.su) & 15) == 0 && p.Hv % 4 == 0 && R % 4 == 0;
   for (int tb = t0; tb < t1; tb += NPF) {
 #pragma unroll
     for (int u = 0; u < NPF; ++u) {
@@ -234,14 +239,24 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
       if (tt < ncap) {
         float* rec = p.su + ((size_t)b * p.cap + tt) * R;
         if (slice == 0 && lane == 0) rec[h] = a;
-        if (write_key) {
-          float* kd = rec + p.Hv + (size_t)hk * DK + row0;
+        float* kd = rec + p.Hv + (size_t)hk * DK + row0;
+        float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;
+        if (vec_rec) {   // every field this lane writes starts on a 16-byte boundary
+          if (write_key) {
 #pragma unroll
-          for (int r = 0; r < RPL; ++r) kd[r] = rk * kr[r];
-        }
-        if (rg == 0) {   // records are only 4-byte aligned in general (R need not be a multiple of 4)
-          float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;
-          dd[0] = d0; dd[1] = d1; dd[2] = d2; dd[3] = d3;
+            for (int r = 0; r < RPL; r += 4)
+              *reinterpret_cast<float4*>(kd + r) =
+                  make_float4(rk * kr[r], rk * kr[r + 1], rk * kr[r + 2], rk * kr[r + 3]);
+          }
+          if (rg == 0) *reinterpret_cast<float4*>(dd) = make_float4(d0, d1, d2, d3);
+        } else {         // records are only 4-byte aligned in general (R need not be a multiple of 4)
+          if (write_key) {
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) kd[r] = rk * kr[r];
+          }
+          if (rg == 0) {
+            dd[0] = d0; dd[1] = d1; dd[2] = d2; dd[3] = d3;
+          }
         }
       }
     }
@@ -255,14 +270,18 @@ __global__ __launch_bounds__(64) void recurrent_step_kernel(DecodeArgs p) {
   }
 }
 
-// Replay of captured records.  Records are fetched RB at a time (all their
-// loads issued before the first is applied) since each application is only two
-// VALU operations per state element.
-constexpr int RB = 8;
+// Replay of captured records.  Records are fetched in batches (all of a
+// batch's loads issued before its first record is applied) since each
+// application is only two VALU operations per state element.  Same slice
+// geometry as the recurrent step.  VEC: every record field this lane reads
+// starts on a 16-byte boundary (the record buffer is 16-byte aligned and Hv and
+// R are multiples of 4), so keys and deltas are read as float4.
+constexpr int RB = 4;   // records per full batch; a tail of 2 and 1 follows
 
-template <int DK>
+template <int DK, bool VEC>
 __global__ __launch_bounds__(64) void replay_kernel(ReplayArgs p) {
   constexpr int RPL = DK / 16;
+  static_assert(!VEC || RPL % 4 == 0, "vector key reads need 4 rows per lane");
   const int lane = threadIdx.x;
   const int cg = lane & 3, rg = lane >> 2;
   int b, h, slice;
@@ -283,23 +302,34 @@ __global__ __launch_bounds__(64) void replay_kernel(ReplayArgs p) {
 
   const size_t R = (size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * dv;
   const float* base = p.su + (size_t)b * p.cap * R;
-  for (int c0 = 0; c0 < m; c0 += RB) {
-    float a[RB];
-    float kk[RB][RPL];
-    float4 d[RB];
+  // N records from c0 on: every load issued, then every application, with no
+  // condition in between (so the loads stay hoisted and in flight together)
+  auto batch = [&](auto nrec, int c0) {
+    constexpr int N = decltype(nrec)::value;
+    float a[N];
+    float kk[N][RPL];
+    float4 d[N];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int c = min(c0 + j, m - 1);   // in-range record; unused copies are discarded
-      const float* rec = base + (size_t)c * R;
+    for (int j = 0; j < N; ++j) {
+      const float* rec = base + (size_t)(c0 + j) * R;
       a[j] = rec[h];
+      const float* kr = rec + p.Hv + (size_t)hk * DK + row0;
+      const float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;
+      if constexpr (VEC) {
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) kk[j][r] = rec[p.Hv + (size_t)hk * DK + row0 + r];
-      const float* dd = rec + p.Hv + (size_t)p.Hq * DK + (size_t)h * dv + col;   // 4-byte aligned only
-      d[j] = make_float4(dd[0], dd[1], dd[2], dd[3]);
+        for (int r = 0; r < RPL; r += 4) {
+          const float4 k4 = *reinterpret_cast<const float4*>(kr + r);
+          kk[j][r] = k4.x; kk[j][r + 1] = k4.y; kk[j][r + 2] = k4.z; kk[j][r + 3] = k4.w;
+        }
+        d[j] = *reinterpret_cast<const float4*>(dd);
+      } else {   // 4-byte aligned only
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) kk[j][r] = kr[r];
+        d[j] = make_float4(dd[0], dd[1], dd[2], dd[3]);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      if (c0 + j >= m) break;
+    for (int j = 0; j < N; ++j) {
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
         const float k = kk[j][r];
@@ -310,7 +340,14 @@ __global__ __launch_bounds__(64) void replay_kernel(ReplayArgs p) {
         S[r].w = fmaf(k, d[j].w, a[j] * S[r].w);
       }
     }
+  };
+  int c = 0;
+  for (; c + RB <= m; c += RB) batch(std::integral_constant<int, RB>{}, c);
+  if (m - c >= 2) {
+    batch(std::integral_constant<int, 2>{}, c);
+    c += 2;
   }
+  if (m - c >= 1) batch(std::integral_constant<int, 1>{}, c);
 #pragma unroll
   for (int r = 0; r < RPL; ++r) store_state4(st + (size_t)(row0 + r) * dv + col, S[r]);
 }
@@ -371,13 +408,23 @@ hipError_t launch_recurrent(DType dt, const DecodeArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int DK, bool VEC>
+static hipError_t launch_replay_v(const ReplayArgs& a, hipStream_t s) {
+  prof_begin(K_REPLAY, s);
+  hipLaunchKernelGGL((replay_kernel<DK, VEC>), dim3(slice_grid(a.B, a.Hv, a.dv)), dim3(64), 0, s, a);
+  prof_end(K_REPLAY, s);
+  return hipGetLastError();
+}
+
 template <int DK>
 static hipError_t launch_replay_dk(const ReplayArgs& a, hipStream_t s) {
   if (a.B == 0 || a.cap == 0) return hipSuccess;
-  prof_begin(K_REPLAY, s);
-  hipLaunchKernelGGL((replay_kernel<DK>), dim3(slice_grid(a.B, a.Hv, a.dv)), dim3(64), 0, s, a);
-  prof_end(K_REPLAY, s);
-  return hipGetLastError();
+  const size_t R = (size_t)a.Hv + (size_t)a.Hq * DK + (size_t)a.Hv * a.dv;
+  const bool vec = (reinterpret_cast<uintptr_t>(a.su) & 15) == 0 && a.Hv % 4 == 0 && R % 4 == 0;
+  if constexpr (DK >= 64) {
+    if (vec) return launch_replay_v<DK, true>(a, s);
+  }
+  return launch_replay_v<DK, false>(a, s);
 }
 
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t s) {

@@ -92,16 +92,19 @@ def test_draft_accept_replay_equals_non_speculative(gdn, dtype):
     assert torch.equal(o_a, o_b) and torch.equal(s_a, s_b)
 
 
-def test_ragged_draft_with_capture_limits(gdn):
+# Record layouts: R = Hv + Hq dk + Hv dv a multiple of 4 with Hv too (16-byte
+# record fields), or not (4-byte fields); 32- and 16-column replay slices.
+@pytest.mark.parametrize("Hq,Hv,dk,dv", [(2, 4, 128, 64), (1, 3, 64, 32), (2, 6, 32, 32),
+                                         (2, 4, 64, 16), (1, 1, 16, 16)])
+def test_ragged_draft_with_capture_limits(gdn, Hq, Hv, dk, dv):
     """Ragged drafts packed by cu_seqlens, capture counts below, at and above the
     row length and the capacity: replaying what was captured reproduces the
     non-speculative state after that many tokens."""
     lengths = [5, 1, 7, 3, 6]
     counts = [2, 1, 9, 0, 6]          # clamped to min(count, capacity, length)
     cap = 6
-    Hq, Hv, dk, dv = 2, 4, 128, 64
-    case = gi.random_case(5150, lengths, Hq=Hq, Hv=Hv, dk=dk, dv=dv, dtype="bf16")
-    say(f"case ragged speculative lengths={lengths} counts={counts} cap={cap}")
+    case = gi.random_case(5150 + dk + dv + Hv, lengths, Hq=Hq, Hv=Hv, dk=dk, dv=dv, dtype="bf16")
+    say(f"case ragged speculative Hq={Hq} Hv={Hv} dk={dk} dv={dv} lengths={lengths} counts={counts} cap={cap}")
     c = to_dev(case)
     args = [c[x] for x in ("q", "k", "v", "g", "beta")]
     cnt = torch.tensor(counts, dtype=torch.int32, device=c["s0"].device)
@@ -118,7 +121,7 @@ def test_ragged_draft_with_capture_limits(gdn):
             assert torch.equal(state[b].cpu(), case["s0"][b])
             continue
         rows = slice(cu[b], cu[b] + m)
-        sub = {x: c[x][rows] for x in ("q", "k", "v", "g", "beta")}
+        sub = {x: c[x][rows].clone() for x in ("q", "k", "v", "g", "beta")}   # fresh, aligned storage
         _, ref_state, _ = gdn.gdn_recurrent_step(sub["q"][None], sub["k"][None], sub["v"][None],
                                                  sub["g"][None], sub["beta"][None], scale=case["scale"],
                                                  initial_state=c["s0"][b:b + 1].contiguous())
