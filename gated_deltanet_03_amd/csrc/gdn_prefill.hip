@@ -517,7 +517,9 @@ __global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) voi
 //
 //    Chunk inputs are staged with direct global->LDS loads (one wave
 //    instruction writes 64 lanes x 16 bytes contiguously at a wave-uniform LDS
-//    address), double-buffered so chunk c+1 streams in while chunk c computes.
+//    address), double-buffered so chunk c+1 streams in while chunk c computes;
+//    with dedicated load-issuing waves and room for a third stage, chunks c+1
+//    and c+2 are both in flight, so a load has two chunk steps to land.
 //    Row-major tiles are XOR-swizzled per 16-byte piece (piece p of row r lives
 //    at piece p ^ (r mod pieces-per-row)) so fragment reads of 16 consecutive
 //    rows hit distinct banks.  Rows past a sequence's end are loaded from its
@@ -572,8 +574,10 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
 }
 
 // LDS plan of the state kernel.  TR: K^T comes from transpose reads, so no K^T
-// region.
-template <typename T, int DK, int NG, bool TR>
+// region.  DED: dedicated load-issuing waves, which keep chunk inputs three
+// stages deep when they fit (two chunks in flight while one is computed), else
+// two; chain-issued loads use at most two.
+template <typename T, int DK, int NG, bool TR, bool DED>
 struct StateSmem {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int SW = 16 * NG;                // columns per workgroup (NG groups of 16)
@@ -592,7 +596,7 @@ struct StateSmem {
   static constexpr int SXB = NG * NSB * FB;         // state fragments, one set per column group
   static constexpr int DXB = NG * 2 * FB;           // Delta fragments, one set per column group
   static constexpr int FIXED = KTB + SXB + DXB;
-  static constexpr int NBUF = 2 * STAGE + FIXED <= 160 * 1024 ? 2 : 1;
+  static constexpr int NBUF = (DED && 3 * STAGE + FIXED <= 160 * 1024) ? 3 : (2 * STAGE + FIXED <= 160 * 1024 ? 2 : 1);
   static constexpr size_t total = (size_t)NBUF * STAGE + FIXED;
   // byte offsets inside one stage buffer
   static constexpr int OK_ = 0, OQ = KB, OV = 2 * KB, OA = 2 * KB + VB, OG = 2 * KB + VB + AB;
@@ -604,7 +608,9 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   // 16-token tiles of each 32-token block present); else built by the output
   // waves with permutation products
   constexpr bool TRK = sizeof(T) == 2 && DK == 128 && C >= 32;
-  using SM = StateSmem<T, DK, NG, TRK>;
+  // three stages need dedicated loaders; the state-emitting variant keeps two
+  // (the third costs it a register spill)
+  using SM = StateSmem<T, DK, NG, TRK, (NDW > 0 && !EMIT)>;
   constexpr int SW = SM::SW;
   constexpr int nrt = C / 16;
   constexpr int NST = SM::NST, NSB = SM::NSB, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
@@ -679,6 +685,21 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     vrow[m] = r;
     vvo[m] = (uint32_t)(((r * p.Hv + h) * dv + SW * slice + pp * PER) * ES);
   }
+  // Fewest DMA instructions any issuing wave puts in flight per chunk (K, Q and
+  // A'/MP slots; V and the factor vector counted as none).  With three stage
+  // buffers an issuer waits for chunk c with vmcnt(LB): loads return in issue
+  // order, so at most LB outstanding leaves none of chunk c's.
+  constexpr int LB = [] {
+    int mn = 63;
+    for (int w = 0; w < NG; ++w) {
+      int n = 0;
+      for (int m = 0; m < KPW; ++m) n += (w + NG * m < PPR) ? 2 : 0;
+      for (int m = 0; m < APW; ++m) n += (w + NG * m < NA) ? 1 : 0;
+      mn = n < mn ? n : mn;
+    }
+    return mn;
+  }();
+  static_assert(LB >= 0 && LB <= 63, "vmcnt immediate");
   const int kq_row_stride = p.Hq * DK, v_row_stride = p.Hv * dv;
   auto issue = [&](int c, int buf) {
     const int t0 = st0 + c * C;
@@ -781,6 +802,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     }
   }
   if (issuer && nch > 0) issue(0, 0);
+  if (SM::NBUF == 3 && issuer && nch > 1) issue(1, 1);
 
   // B fragment selecting the 16 columns of this group out of a 32-slot V row
   // fragment (slots 8g + j, g < 2, read columns 16 wq + 8g + j): V times it is
@@ -810,14 +832,22 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   const size_t olane = (size_t)(4 * g4) * ostride + (size_t)h * dv + col0 + i16;
 
   for (int c = 0; c < nch; ++c) {
-    const int buf = SM::NBUF == 2 ? (c & 1) : 0;
+    const int buf = SM::NBUF == 3 ? c % 3 : (SM::NBUF == 2 ? (c & 1) : 0);
     const int t0 = st0 + c * C;
     const int len = min(C, st1 - t0);
     // chunk c has landed (the issuing waves wait for their own loads); chunk c-1
     // buffers are free
-    if (issuer) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (issuer) {
+      if (SM::NBUF == 3 && c + 1 < nch)
+        __builtin_amdgcn_s_waitcnt((LB & 15) | (7 << 4) | (15 << 8) | ((LB >> 4) << 14));   // vmcnt(LB)
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     lds_barrier();
-    if (dmaw && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
+    if (dmaw && SM::NBUF >= 2) {   // three stages: chunk c+2 into the buffer of chunk c-1, now free
+      const int cn = c + SM::NBUF - 1;
+      if (cn < nch) issue(cn, SM::NBUF == 3 ? cn % 3 : buf ^ 1);
+    }
     const unsigned char* sb = smem_raw + buf * SM::STAGE;
     const unsigned char* Kt = sb + SM::OK_;
     const unsigned char* Qt = sb + SM::OQ;
@@ -1095,7 +1125,7 @@ static int device_cus() {
 
 template <typename T, int DK, int C, int NG, int NDW, bool EMIT>
 static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
-  using SM = StateSmem<T, DK, NG, sizeof(T) == 2 && DK == 128 && C >= 32>;
+  using SM = StateSmem<T, DK, NG, sizeof(T) == 2 && DK == 128 && C >= 32, (NDW > 0 && !EMIT)>;
   const size_t sm2 = SM::total;
   if (sm2 > 160 * 1024) return hipErrorInvalidValue;
   static bool attr = false;
