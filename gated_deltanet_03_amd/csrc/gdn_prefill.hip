@@ -1,7 +1,9 @@
-// Chunked GDN prefill on gfx950: three launches on the caller's stream.
+// Chunked GDN prefill on gfx950: two or three launches on the caller's stream.
 //
 //  1. chunk_plan_kernel   per-sequence chunk offsets (exclusive scan of
-//                         ceil(len_s / C)) into the workspace header.
+//                         ceil(len_s / C)) into the workspace header; only for
+//                         more than 64 sequences (below that every wave of
+//                         kernels 2 and 3 scans the lengths itself).
 //  2. chunk_prep_kernel   fully parallel over (chunk, key head): everything that
 //                         does not depend on the carried state.
 //  3. chunk_state_kernel  parallel over (sequence, value head, column slice),
@@ -102,6 +104,45 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(PrefillArgs p) {
     p.chunk_info[2 * c] = a;
     p.chunk_info[2 * c + 1] = n;
   }
+}
+
+// The same plan for at most 64 sequences, computed by one wave at the start of
+// the prep and state kernels (which then need no plan launch): lane s < B gets
+// the saturated exclusive chunk offset of sequence s, every lane the saturated
+// chunk total.  Offsets, totals and the chunk -> (first token, length) map are
+// those chunk_plan_kernel writes.
+constexpr int kWavePlanMaxSeqs = 64;
+
+template <int C>
+__device__ __forceinline__ void wave_plan(const PrefillArgs& p, int lane, int& excl, int& total) {
+  int n = 0;
+  if (lane < p.B) {
+    int t0, t1;
+    seq_range(p.cu, p.T, p.total, lane, t0, t1);
+    n = (t1 - t0 + C - 1) / C;
+  }
+  int x = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  excl = min(x - n, p.max_chunks);
+  total = min(__shfl(x, 63), p.max_chunks);
+}
+
+// First token and length of global chunk gc from a wave plan (length 0 past the
+// last chunk): its sequence is the last s with offset <= gc.
+template <int C>
+__device__ __forceinline__ int2 wave_plan_chunk(const PrefillArgs& p, int lane, int excl, int total, int gc) {
+  if (gc >= total) return make_int2(0, 0);
+  const unsigned long long m = __ballot(lane < p.B && excl <= gc);
+  const int s = 63 - __clzll((long long)m);
+  const int off = __shfl(excl, s);
+  int t0, t1;
+  seq_range(p.cu, p.T, p.total, s, t0, t1);
+  const int a = t0 + (gc - off) * C;
+  return make_int2(a, min(C, t1 - a));
 }
 
 template <typename T>
@@ -250,10 +291,17 @@ __global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) voi
   const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (item >= nitems) return;
   const int gc = item / npairs, h0 = (item % npairs) * HPW;
-  const int2 info = reinterpret_cast<const int2*>(p.chunk_info)[gc];
-  const int t0 = info.x, len = info.y;
-  if (len <= 0) return;
   const int lane = threadIdx.x;
+  int2 info;
+  if (p.B <= kWavePlanMaxSeqs) {
+    int excl, total;
+    wave_plan<C>(p, lane, excl, total);
+    info = wave_plan_chunk<C>(p, lane, excl, total, gc);
+  } else {
+    info = reinterpret_cast<const int2*>(p.chunk_info)[gc];
+  }
+  const int t0 = __builtin_amdgcn_readfirstlane(info.x), len = __builtin_amdgcn_readfirstlane(info.y);
+  if (len <= 0) return;
   const int i16 = lane & 15, g4 = lane >> 4;
   const int hk = h0 / (p.Hv / p.Hq);
 
@@ -655,8 +703,17 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
 
   int st0, st1;
   seq_range(p.cu, p.T, p.total, s, st0, st1);
-  const int cbeg = p.chunk_offsets[s];
-  const int nch = p.chunk_offsets[s + 1] - cbeg;
+  int cbeg, nch;
+  if (p.B <= kWavePlanMaxSeqs) {
+    int excl, total;
+    wave_plan<C>(p, lane, excl, total);
+    // wave-uniform by construction; readfirstlane keeps them in scalar registers
+    cbeg = __builtin_amdgcn_readfirstlane(__shfl(excl, s));
+    nch = __builtin_amdgcn_readfirstlane((s + 1 < p.B ? __shfl(excl, s + 1) : total)) - cbeg;
+  } else {
+    cbeg = p.chunk_offsets[s];
+    nch = p.chunk_offsets[s + 1] - cbeg;
+  }
 
   const T* kp = static_cast<const T*>(p.k);
   const T* qp = static_cast<const T*>(p.q);
@@ -1148,11 +1205,14 @@ static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
 
 template <typename T, int DK, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  prof_begin(K_PLAN, st);
-  hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a);
-  prof_end(K_PLAN, st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // up to 64 sequences the prep and state kernels plan for themselves
+  hipError_t e = hipSuccess;
+  if (a.B > kWavePlanMaxSeqs) {
+    prof_begin(K_PLAN, st);
+    hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a);
+    prof_end(K_PLAN, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.max_chunks > 0) {
     // value heads in pairs when pairs share a key head (Hv / Hq even)
     const bool pairs = ((a.Hv / a.Hq) % 2) == 0;

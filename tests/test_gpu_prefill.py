@@ -184,3 +184,43 @@ def test_prefill_many_rows_geometry(gdn, dtype, C):
                                        cu_seqlens=d["cu_seqlens"], chunk_size=C, initial_state=d["s0"])
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(fin, fin2)
+
+
+@pytest.mark.parametrize("nseq", [64, 70])
+def test_prefill_many_sequences_plan(gdn, nseq):
+    """Up to 64 sequences the prep and state kernels build the chunk plan
+    themselves; beyond that a plan kernel writes it to the workspace.  Both
+    sides of the limit, with empty and ragged sequences, boundary states
+    included."""
+    lengths = [(7 * i) % 45 if i % 9 else 0 for i in range(nseq)]
+    lengths[nseq // 2] = 130                         # one sequence over several chunks
+    C = 32
+    case = gi.random_case(9700 + nseq, lengths, Hq=1, Hv=2, dk=32, dv=32, dtype="bf16")
+    say(f"case {nseq} sequences, {sum(lengths)} tokens, chunk {C}")
+    d = to_dev(case)
+    args = [d[x] for x in ("q", "k", "v", "g", "beta")]
+    o, fin, cs = gdn.gdn_prefill_chunked_states(*args, scale=case["scale"], cu_seqlens=d["cu_seqlens"], chunk_size=C,
+                                                initial_state=d["s0"])
+    o2, fin2 = gdn.gdn_prefill_chunked(*args, scale=case["scale"], cu_seqlens=d["cu_seqlens"], chunk_size=C,
+                                       initial_state=d["s0"])
+    torch.cuda.synchronize()
+    ref = oracle.recurrent(case["q"], case["k"], case["v"], case["g"], case["beta"], case["scale"], 1, 2,
+                           cu_seqlens=case["cu_seqlens"], initial_state=case["s0"], boundary_every=C)
+    assert_close(o, ref["o"], "bf16", "o")
+    assert_close(fin, ref["final"], "bf16", "final")
+    assert_close(cs, ref["boundary"], "bf16", "chunk states")
+    assert torch.equal(o, o2) and torch.equal(fin, fin2)
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert torch.equal(fin[b].cpu(), case["s0"][b])
+
+
+def test_prefill_many_dense_rows_plan(gdn):
+    """Dense rows (no cu_seqlens) beyond the 64-sequence wave plan."""
+    B, T = 66, 40
+    case = gi.random_case(9800, [T] * B, Hq=1, Hv=2, dk=32, dv=32, dtype="bf16", dense=True)
+    say(f"case dense B={B} T={T}")
+    o, fin = prefill(gdn, case, 32)
+    ref = oracle_run(case)
+    assert_close(o, ref["o"], "bf16", "o")
+    assert_close(fin, ref["final"], "bf16", "final")
