@@ -20,6 +20,9 @@ with every launch bracketed by the library's own HIP-event pairs on the launch
 stream, gives the per-kernel durations (roofline, breakdown); those event pairs
 cost ~2-3 us per launch boundary, so they are kept off the first pass.
 
+Those pairs add ~2 us to a short launch, so the breakdown's decode, replay and
+snapshot times come from back-to-back loops over every state set between one
+event pair (the per-launch figures are kept beside them as us_event_pairs).
 The breakdown also times, outside the step, the prefix-reuse batch: 16 rows x
 256 bf16 tokens continuing from one broadcast snapshot of a 4096-token prefix
 (event-timed loop over two distinct resident batches), without and with the
@@ -308,6 +311,30 @@ def main():
     # 4096-token prefix, without and with the rows' final states.
     batch = _prefix_batch(gdn, gi, dev, C, args.steps)
 
+    # Timed region 4 (breakdown): the short launches back to back, one event pair
+    # around a loop over every state set (each call's state is cold), so their
+    # per-call times carry no per-launch event cost.
+    def loop_us(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / n
+
+    def dec_call(i):
+        gdn.gdn_recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
+                               initial_state=states[i % STATE_SETS], cu_seqlens=d["cu_seqlens"], o=dec_o,
+                               final_state=finals[i % STATE_SETS], state_update_capacity=cap,
+                               capture_count=counts, state_update_active=1, state_update=su)
+
+    loop = {"decode": loop_us(dec_call, 2 * STATE_SETS),
+            "replay": loop_us(lambda i: gdn.gdn_replay_state_updates(states[i % STATE_SETS], su, accept, Hq=Hq),
+                              2 * STATE_SETS),
+            "snapshot": loop_us(lambda i: gdn.gdn_state_snapshot(fins[i % 2], snaps[i % 2]), 2 * STATE_SETS)}
+
     # Untimed: one plain copy of a cold 256 MiB buffer (the largest copy_kernel
     # dispatch of the command), whose FETCH_SIZE / WRITE_SIZE readings calibrate
     # the HBM traffic counters of the other kernels.
@@ -324,9 +351,12 @@ def main():
     pbytes = prefill_bytes(pre["T"], N, Hq, Hv, dk, dv, es)
     t_prefill_us = sum(per_step_us.get(k, 0.0) for k in ("chunk_plan_kernel", "chunk_prep_kernel",
                                                           "chunk_state_kernel"))
-    t_dec_us = per_step_us.get("recurrent_step_kernel", float("nan"))
-    t_rep_us = per_step_us.get("replay_kernel", float("nan"))
-    t_snap_us = per_step_us.get("copy_kernel", float("nan"))
+    # short launches: back-to-back loop times (region 4); the per-launch event
+    # pairs of region 2 are reported beside them
+    t_dec_us, t_rep_us, t_snap_us = loop["decode"], loop["replay"], loop["snapshot"]
+    ev_us = {k: per_step_us.get(n, float("nan")) for k, n in (("decode", "recurrent_step_kernel"),
+                                                              ("replay", "replay_kernel"),
+                                                              ("snapshot", "copy_kernel"))}
 
     breakdown = {
         "prefill": {"us": t_prefill_us, "tokens_per_s": pre["T"] / (t_prefill_us * 1e-6),
@@ -334,13 +364,16 @@ def main():
                     "mfma_frac": F / (t_prefill_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
                     "algorithmic_mb": pbytes / 1e6,
                     "hbm_frac": pbytes / (t_prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
-        "decode": {"us": t_dec_us, "tokens": dec["T"], "algorithmic_mb": dbytes / 1e6,
+        "decode": {"us": t_dec_us, "us_event_pairs": ev_us["decode"], "tokens": dec["T"],
+                   "algorithmic_mb": dbytes / 1e6,
                    "gbs": dbytes / (t_dec_us * 1e-6) / 1e9,
                    "hbm_frac": dbytes / (t_dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
-        "replay": {"us": t_rep_us, "records": sum(n_cap), "algorithmic_mb": rbytes / 1e6,
+        "replay": {"us": t_rep_us, "us_event_pairs": ev_us["replay"], "records": sum(n_cap),
+                   "algorithmic_mb": rbytes / 1e6,
                    "gbs": rbytes / (t_rep_us * 1e-6) / 1e9,
                    "hbm_frac": rbytes / (t_rep_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
-        "snapshot": {"us": t_snap_us, "gbs": 2 * N * Hv * dk * dv * 4 / (t_snap_us * 1e-6) / 1e9},
+        "snapshot": {"us": t_snap_us, "us_event_pairs": ev_us["snapshot"],
+                     "gbs": 2 * N * Hv * dk * dv * 4 / (t_snap_us * 1e-6) / 1e9},
         "prefix_batch": batch,
     }
 
