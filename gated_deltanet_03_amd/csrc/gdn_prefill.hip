@@ -758,7 +758,9 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   }();
   static_assert(LB >= 0 && LB <= 63, "vmcnt immediate");
   const int kq_row_stride = p.Hq * DK, v_row_stride = p.Hv * dv;
-  auto issue = [&](int c, int buf) {
+  // part 0: every load of chunk c; 1: the K and Q tiles; 2: V, A'/MP and the
+  // factor vector
+  auto issue = [&](int c, int buf, int part) {
     const int t0 = st0 + c * C;
     const int last = min(C, st1 - t0) - 1;
     unsigned char* sb = smem_raw + buf * SM::STAGE;
@@ -768,7 +770,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     Block<T> blk(p.chunk_data, (size_t)(cbeg + c), p.Hv, h);
     if (last == C - 1) {   // full chunk: no row needs clamping
 #pragma unroll
-      for (int m = 0; m < KPW; ++m) {
+      for (int m = 0; m < KPW && part != 2; ++m) {
         const int j = wq + NG * m;
         if (j < PPR) {
           dma16(kc + kvo[m], sb + SM::OK_ + j * 1024);
@@ -776,13 +778,13 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         }
       }
 #pragma unroll
-      for (int m = 0; m < VPW; ++m) {
+      for (int m = 0; m < VPW && part != 1; ++m) {
         const int j = wq + NG * m;
         if (j < pprv) dma16(vc + vvo[m], sb + SM::OV + j * 1024);
       }
     } else {               // last chunk of a sequence: rows past its end repeat its last row
 #pragma unroll
-      for (int m = 0; m < KPW; ++m) {
+      for (int m = 0; m < KPW && part != 2; ++m) {
         const int j = wq + NG * m;
         if (j < PPR) {
           const int64_t d = (int64_t)(min(krow[m], last) - krow[m]) * kq_row_stride * ES;
@@ -791,7 +793,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         }
       }
 #pragma unroll
-      for (int m = 0; m < VPW; ++m) {
+      for (int m = 0; m < VPW && part != 1; ++m) {
         const int j = wq + NG * m;
         if (j < pprv) dma16(vc + vvo[m] + (int64_t)(min(vrow[m], last) - vrow[m]) * v_row_stride * ES,
                             sb + SM::OV + j * 1024);
@@ -799,11 +801,11 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     }
     const char* ab = reinterpret_cast<const char*>(blk.A);
 #pragma unroll
-    for (int m = 0; m < APW; ++m) {
+    for (int m = 0; m < APW && part != 1; ++m) {
       const int j = wq + NG * m;
       if (j < NA) dma16(ab + (uint32_t)((j * 64 + lane) * 16), sb + SM::OA + j * 1024);
     }
-    if (wq == NG - 1) dma16(reinterpret_cast<const char*>(blk.gk) + 16 * lane, sb + SM::OG);
+    if (part != 1 && wq == NG - 1) dma16(reinterpret_cast<const char*>(blk.gk) + 16 * lane, sb + SM::OG);
   };
 
 
@@ -858,8 +860,36 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
     }
   }
-  if (issuer && nch > 0) issue(0, 0);
-  if (SM::NBUF == 3 && issuer && nch > 1) issue(1, 1);
+  // an issuing wave's wait for chunk c to land in LDS
+  auto wait_chunk = [&](int c) {
+    if (SM::NBUF == 3 && c + 1 < nch)
+      __builtin_amdgcn_s_waitcnt((LB & 15) | (7 << 4) | (15 << 8) | ((LB >> 4) << 14));   // vmcnt(LB)
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  if (issuer && nch > 0) issue(0, 0, 0);
+  if (SM::NBUF == 3 && issuer && nch > 1) issue(1, 1, 0);
+  if constexpr (NDW > 0) {
+    // Load-issuing waves run a loop of their own with the same workgroup
+    // barriers per chunk as the compute waves (TOP, MID, and a third with a
+    // single stage buffer), so none of their state is live in the compute
+    // waves' loop.  With three stages, chunk c+2 goes into the buffer of chunk
+    // c-1, free after TOP.
+    if (dmaw) {
+      for (int c = 0; c < nch; ++c) {
+        wait_chunk(c);
+        lds_barrier();   // TOP
+        const int cn = c + SM::NBUF - 1;
+        if (SM::NBUF >= 2 && cn < nch) issue(cn, SM::NBUF == 3 ? cn % 3 : (c & 1) ^ 1, 0);
+        lds_barrier();   // MID
+        if constexpr (SM::NBUF == 1) {
+          lds_barrier();
+          if (c + 1 < nch) issue(c + 1, 0, 0);
+        }
+      }
+      return;
+    }
+  }
 
   // B fragment selecting the 16 columns of this group out of a 32-slot V row
   // fragment (slots 8g + j, g < 2, read columns 16 wq + 8g + j): V times it is
@@ -894,17 +924,8 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     const int len = min(C, st1 - t0);
     // chunk c has landed (the issuing waves wait for their own loads); chunk c-1
     // buffers are free
-    if (issuer) {
-      if (SM::NBUF == 3 && c + 1 < nch)
-        __builtin_amdgcn_s_waitcnt((LB & 15) | (7 << 4) | (15 << 8) | ((LB >> 4) << 14));   // vmcnt(LB)
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    if (NDW == 0 && issuer) wait_chunk(c);
     lds_barrier();
-    if (dmaw && SM::NBUF >= 2) {   // three stages: chunk c+2 into the buffer of chunk c-1, now free
-      const int cn = c + SM::NBUF - 1;
-      if (cn < nch) issue(cn, SM::NBUF == 3 ? cn % 3 : buf ^ 1);
-    }
     const unsigned char* sb = smem_raw + buf * SM::STAGE;
     const unsigned char* Kt = sb + SM::OK_;
     const unsigned char* Qt = sb + SM::OQ;
@@ -954,7 +975,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       for (int r = 0; r < nrt; ++r) av[r] = v_frag(Vs, 16 * r + i16);
       if constexpr (NSB > 1) load_kblock(1);
       __builtin_amdgcn_sched_barrier(0);
-      if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
+      if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1, 0);
       __builtin_amdgcn_sched_barrier(0);
       f32x4 KSa[4], Va[4];
 #pragma unroll
@@ -1152,7 +1173,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       // single stage buffer: chunk c+1 may only overwrite it once every wave is
       // done reading chunk c (gamma, tail and MP are read after MID)
       lds_barrier();
-      if (issuer && c + 1 < nch) issue(c + 1, 0);
+      if (NDW == 0 && issuer && c + 1 < nch) issue(c + 1, 0, 0);
     }
   }
 
