@@ -32,6 +32,8 @@
 //
 // A' and MP are written in fragment-native order (gdn_mfma.h), lower-triangular
 // 16x32 blocks only: block (r, kb) with kb <= r/2, i.e. 6 blocks per matrix.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
@@ -918,264 +920,273 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   const size_t ostride = (size_t)p.Hv * dv;
   const size_t olane = (size_t)(4 * g4) * ostride + (size_t)h * dv + col0 + i16;
 
-  for (int c = 0; c < nch; ++c) {
-    const int buf = SM::NBUF == 3 ? c % 3 : (SM::NBUF == 2 ? (c & 1) : 0);
-    const int t0 = st0 + c * C;
-    const int len = min(C, st1 - t0);
-    // chunk c has landed (the issuing waves wait for their own loads); chunk c-1
-    // buffers are free
-    if (NDW == 0 && issuer) wait_chunk(c);
-    lds_barrier();
-    const unsigned char* sb = smem_raw + buf * SM::STAGE;
-    const unsigned char* Kt = sb + SM::OK_;
-    const unsigned char* Qt = sb + SM::OQ;
-    const unsigned char* Vs = sb + SM::OV;
-    const T* AMP = reinterpret_cast<const T*>(sb + SM::OA);
-    const float* GT = reinterpret_cast<const float*>(sb + SM::OG);
-    f32x4 QSa[4];
-    Frag<T> Tb0, Tb1;
-    // K^T fragment (state tile rt, token block kb): for state row 16rt + n,
-    // K[32kb + 4g + j][dk(16rt + n)] in slots j < 4 and the same 16 tokens later
-    // in slots 4..7.  With transpose reads, lane s of each 16-lane group
-    // addresses row 32kb + 4g + s/4 (+16), dk columns 32(rt/2) + 8(s%4) +
-    // 4(rt%2) .. +3 of the K tile, whose column block is perm_dk's.
-    auto kt_frag = [&](int rt, int kb) {
-      if constexpr (TRK) {
-        const int piece = 4 * (rt >> 1) + (i16 & 3);
-        const int r0 = 32 * kb + 4 * g4 + (i16 >> 2), r1 = r0 + 16;
-        const s16x4 a = lds_read_tr16(Kt + r0 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r0)) << 4) + 8 * (rt & 1));
-        const s16x4 b = lds_read_tr16(Kt + r1 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r1)) << 4) + 8 * (rt & 1));
-        const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
-        Frag<T> f;
-        f.v = __builtin_bit_cast(decltype(f.v), make_uint4(ua.x, ua.y, ub.x, ub.y));
-        return f;
-      } else {
-        return load_frag_native<T>(KT + ((2 * rt + kb) * 64 + lane) * 8);
-      }
-    };
-    // K^T fragments are read LA ahead of the state-update products that use
-    // them; with transpose reads the first LA are issued before MID
-    constexpr int NKB2 = nrt > 2 ? 2 : 1, NU = NKB2 * NST, LA = TRK ? 7 : 8;
-    Frag<T> kt[NU];
-    float gl = 0.f;
-    if (chain) {
-      // ---- LDS reads and products in a fixed interleave: at most ~14 reads in
-      //      flight (the LDS counter a wait can name stops at 15), K blocks two
-      //      ahead of the products that use them, and gamma, A' and tail
-      //      prefetched behind the last K block ----------------------------------
-      constexpr int X1 = NSB >= 2 ? NSB - 2 : 0;   // step that prefetches gamma and A'
-      Frag<T> ak[NSB][nrt], av[nrt], aa[NTRI];
-      f32x4 gm[4], tl[4];
-      auto load_kblock = [&](int kb) {
-#pragma unroll
-        for (int r = 0; r < nrt; ++r) ak[kb][r] = kq_frag(Kt, 16 * r + i16, kb);
+  // The chunk loop, compiled separately for chain waves (CH) and output waves so
+  // that neither role's values are live in the other's loop; both meet at the
+  // same barriers.
+  auto chunk_loop = [&](auto role) {
+    constexpr bool CH = decltype(role)::value;
+    for (int c = 0; c < nch; ++c) {
+      const int buf = SM::NBUF == 3 ? c % 3 : (SM::NBUF == 2 ? (c & 1) : 0);
+      const int t0 = st0 + c * C;
+      const int len = min(C, st1 - t0);
+      // chunk c has landed (the issuing waves wait for their own loads); chunk c-1
+      // buffers are free
+      if (NDW == 0 && CH) wait_chunk(c);
+      lds_barrier();
+      const unsigned char* sb = smem_raw + buf * SM::STAGE;
+      const unsigned char* Kt = sb + SM::OK_;
+      const unsigned char* Qt = sb + SM::OQ;
+      const unsigned char* Vs = sb + SM::OV;
+      const T* AMP = reinterpret_cast<const T*>(sb + SM::OA);
+      const float* GT = reinterpret_cast<const float*>(sb + SM::OG);
+      f32x4 QSa[4];
+      Frag<T> Tb0, Tb1;
+      // K^T fragment (state tile rt, token block kb): for state row 16rt + n,
+      // K[32kb + 4g + j][dk(16rt + n)] in slots j < 4 and the same 16 tokens later
+      // in slots 4..7.  With transpose reads, lane s of each 16-lane group
+      // addresses row 32kb + 4g + s/4 (+16), dk columns 32(rt/2) + 8(s%4) +
+      // 4(rt%2) .. +3 of the K tile, whose column block is perm_dk's.
+      auto kt_frag = [&](int rt, int kb) {
+        if constexpr (TRK) {
+          const int piece = 4 * (rt >> 1) + (i16 & 3);
+          const int r0 = 32 * kb + 4 * g4 + (i16 >> 2), r1 = r0 + 16;
+          const s16x4 a = lds_read_tr16(Kt + r0 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r0)) << 4) + 8 * (rt & 1));
+          const s16x4 b = lds_read_tr16(Kt + r1 * SM::ROWB + ((piece ^ kq_swz<PPR, TRK>(r1)) << 4) + 8 * (rt & 1));
+          const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+          Frag<T> f;
+          f.v = __builtin_bit_cast(decltype(f.v), make_uint4(ua.x, ua.y, ub.x, ub.y));
+          return f;
+        } else {
+          return load_frag_native<T>(KT + ((2 * rt + kb) * 64 + lane) * 8);
+        }
       };
-      load_kblock(0);
+      // K^T fragments are read LA ahead of the state-update products that use
+      // them; with transpose reads the first LA are issued before MID
+      constexpr int NKB2 = nrt > 2 ? 2 : 1, NU = NKB2 * NST, LA = TRK ? 7 : 8;
+      Frag<T> kt[NU];
+      float gl = 0.f;
+      if constexpr (CH) {
+        // ---- LDS reads and products in a fixed interleave: at most ~14 reads in
+        //      flight (the LDS counter a wait can name stops at 15), K blocks two
+        //      ahead of the products that use them, and gamma, A' and tail
+        //      prefetched behind the last K block ----------------------------------
+        constexpr int X1 = NSB >= 2 ? NSB - 2 : 0;   // step that prefetches gamma and A'
+        Frag<T> ak[NSB][nrt], av[nrt], aa[NTRI];
+        f32x4 gm[4], tl[4];
+        auto load_kblock = [&](int kb) {
 #pragma unroll
-      for (int r = 0; r < nrt; ++r) av[r] = v_frag(Vs, 16 * r + i16);
-      if constexpr (NSB > 1) load_kblock(1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 KSa[4], Va[4];
+          for (int r = 0; r < nrt; ++r) ak[kb][r] = kq_frag(Kt, 16 * r + i16, kb);
+        };
+        load_kblock(0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) KSa[r] = Va[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < nrt; ++r) av[r] = v_frag(Vs, 16 * r + i16);
+        if constexpr (NSB > 1) load_kblock(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 KSa[4], Va[4];
 #pragma unroll
-      for (int kb = 0; kb < NSB; ++kb) {
+        for (int r = 0; r < 4; ++r) KSa[r] = Va[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < nrt; ++r) mma<T>(KSa[r], ak[kb][r], Sb[kb]);
-        if (kb == 0) {
+        for (int kb = 0; kb < NSB; ++kb) {
 #pragma unroll
-          for (int r = 0; r < nrt; ++r) mma<T>(Va[r], av[r], vsel);
+          for (int r = 0; r < nrt; ++r) mma<T>(KSa[r], ak[kb][r], Sb[kb]);
+          if (kb == 0) {
+#pragma unroll
+            for (int r = 0; r < nrt; ++r) mma<T>(Va[r], av[r], vsel);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (kb + 2 < NSB) load_kblock(kb + 2);
+          if (kb == X1) {
+#pragma unroll
+            for (int r = 0; r < nrt; ++r) gm[r] = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < nrt; ++r) aa[tri_idx(r, 0)] = load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8);
+#pragma unroll
+            for (int r = 2; r < nrt; ++r) aa[tri_idx(r, 1)] = load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8);
+          }
+          if (kb == NSB - 1) {
+#pragma unroll
+            for (int r = 0; r < nrt; ++r) tl[r] = *reinterpret_cast<const f32x4*>(GT + 64 + 16 * r + 4 * g4);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- X = V - gamma * KS ------------------------------------------------
+        f32x4 X[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          X[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (r < nrt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) X[r][q] = Va[r][q] - gm[r][q] * KSa[r][q];
+          }
+        }
+        const Frag<T> Xb0 = make_frag<T>(X[0], X[1]), Xb1 = make_frag<T>(X[2], X[3]);
+        // ---- Delta = A' X --------------------------------------------------------
+        f32x4 D[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          D[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (r < nrt) mma<T>(D[r], aa[tri_idx(r, 0)], Xb0);
+        }
+#pragma unroll
+        for (int r = 2; r < nrt; ++r) mma<T>(D[r], aa[tri_idx(r, 1)], Xb1);
+        if constexpr (TRK) {   // the K tile is complete since TOP: K^T reads overlap Delta's exchange
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
+          gl = GT[192];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        store_frag_native<T>(dx_mine, make_frag<T>(D[0], D[1]));
+        store_frag_native<T>(dx_mine + 512, make_frag<T>(D[2], D[3]));
+        // ---- tail-weighted Delta for the state update ---------------------------
+#pragma unroll
+        for (int r = 0; r < nrt; ++r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) D[r][q] *= tl[r][q];
+        Tb0 = make_frag<T>(D[0], D[1]);
+        Tb1 = make_frag<T>(D[2], D[3]);
+      } else {
+        // ---- QS = Q S (state fragments from the chain wave) ----------------------
+#pragma unroll
+        for (int r = 0; r < 4; ++r) QSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Frag<T> sbf[NSB], aq[NSB][nrt];
+#pragma unroll
+        for (int kb = 0; kb < NSB; ++kb) {
+          sbf[kb] = load_frag_native<T>(sx_mine + kb * 512);
+#pragma unroll
+          for (int r = 0; r < nrt; ++r) aq[kb][r] = kq_frag(Qt, 16 * r + i16, kb);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (kb + 2 < NSB) load_kblock(kb + 2);
-        if (kb == X1) {
 #pragma unroll
-          for (int r = 0; r < nrt; ++r) gm[r] = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+        for (int kb = 0; kb < NSB; ++kb)
 #pragma unroll
-          for (int r = 0; r < nrt; ++r) aa[tri_idx(r, 0)] = load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8);
+          for (int r = 0; r < nrt; ++r) mma<T>(QSa[r], aq[kb][r], sbf[kb]);
+        // ---- K^T fragments: fragment (state tile rt, token block kb) holds, for
+        //      state row 16rt + n, K[32kb + 4g + j][dk(16rt + n)] (lo) and the same
+        //      16 tokens later (hi): tiles D(2kb, rt), D(2kb+1, rt) of K * P, P the
+        //      0/1 matrix picking dk column perm_dk(16rt + n) -------------------------
 #pragma unroll
-          for (int r = 2; r < nrt; ++r) aa[tri_idx(r, 1)] = load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8);
-        }
-        if (kb == NSB - 1) {
+        for (int f0 = 0; f0 < (TRK ? 0 : SM::NKT); f0 += NG) {
+          const int f = f0 + wq;
+          if (f < SM::NKT) {
+            const int rt = f >> 1, kb = f & 1;
+            // B fragment of P: slot 8g + j of the 32-block holding this tile
+            f32x4 plo, phi;
+            if constexpr (DK >= 32) {
+              const int tgt = perm_dk<DK>(16 * rt + i16) - 32 * (rt >> 1);   // dk inside the block
 #pragma unroll
-          for (int r = 0; r < nrt; ++r) tl[r] = *reinterpret_cast<const f32x4*>(GT + 64 + 16 * r + 4 * g4);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // ---- X = V - gamma * KS ------------------------------------------------
-      f32x4 X[4];
+              for (int j = 0; j < 4; ++j) {
+                plo[j] = (8 * g4 + j == tgt) ? 1.f : 0.f;
+                phi[j] = (8 * g4 + 4 + j == tgt) ? 1.f : 0.f;
+              }
+            } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        X[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (r < nrt) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) X[r][q] = Va[r][q] - gm[r][q] * KSa[r][q];
-        }
-      }
-      const Frag<T> Xb0 = make_frag<T>(X[0], X[1]), Xb1 = make_frag<T>(X[2], X[3]);
-      // ---- Delta = A' X --------------------------------------------------------
-      f32x4 D[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        D[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (r < nrt) mma<T>(D[r], aa[tri_idx(r, 0)], Xb0);
-      }
-#pragma unroll
-      for (int r = 2; r < nrt; ++r) mma<T>(D[r], aa[tri_idx(r, 1)], Xb1);
-      if constexpr (TRK) {   // the K tile is complete since TOP: K^T reads overlap Delta's exchange
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
-        gl = GT[192];
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      store_frag_native<T>(dx_mine, make_frag<T>(D[0], D[1]));
-      store_frag_native<T>(dx_mine + 512, make_frag<T>(D[2], D[3]));
-      // ---- tail-weighted Delta for the state update ---------------------------
-#pragma unroll
-      for (int r = 0; r < nrt; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) D[r][q] *= tl[r][q];
-      Tb0 = make_frag<T>(D[0], D[1]);
-      Tb1 = make_frag<T>(D[2], D[3]);
-    } else if (!dmaw) {
-      // ---- QS = Q S (state fragments from the chain wave) ----------------------
-#pragma unroll
-      for (int r = 0; r < 4; ++r) QSa[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      Frag<T> sbf[NSB], aq[NSB][nrt];
-#pragma unroll
-      for (int kb = 0; kb < NSB; ++kb) {
-        sbf[kb] = load_frag_native<T>(sx_mine + kb * 512);
-#pragma unroll
-        for (int r = 0; r < nrt; ++r) aq[kb][r] = kq_frag(Qt, 16 * r + i16, kb);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < NSB; ++kb)
-#pragma unroll
-        for (int r = 0; r < nrt; ++r) mma<T>(QSa[r], aq[kb][r], sbf[kb]);
-      // ---- K^T fragments: fragment (state tile rt, token block kb) holds, for
-      //      state row 16rt + n, K[32kb + 4g + j][dk(16rt + n)] (lo) and the same
-      //      16 tokens later (hi): tiles D(2kb, rt), D(2kb+1, rt) of K * P, P the
-      //      0/1 matrix picking dk column perm_dk(16rt + n) -------------------------
-#pragma unroll
-      for (int f0 = 0; f0 < (TRK ? 0 : SM::NKT); f0 += NG) {
-        const int f = f0 + wq;
-        if (f < SM::NKT) {
-          const int rt = f >> 1, kb = f & 1;
-          // B fragment of P: slot 8g + j of the 32-block holding this tile
-          f32x4 plo, phi;
-          if constexpr (DK >= 32) {
-            const int tgt = perm_dk<DK>(16 * rt + i16) - 32 * (rt >> 1);   // dk inside the block
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              plo[j] = (8 * g4 + j == tgt) ? 1.f : 0.f;
-              phi[j] = (8 * g4 + 4 + j == tgt) ? 1.f : 0.f;
+              for (int j = 0; j < 4; ++j) {
+                plo[j] = (4 * g4 + j == i16) ? 1.f : 0.f;
+                phi[j] = 0.f;
+              }
             }
+            const Frag<T> pf = make_frag<T>(plo, phi);
+            f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+            if (2 * kb < nrt) mma<T>(lo, kq_frag(Kt, 32 * kb + i16, rt >> 1), pf);
+            if (2 * kb + 1 < nrt) mma<T>(hi, kq_frag(Kt, 32 * kb + 16 + i16, rt >> 1), pf);
+            store_frag_native<T>(KT + (f * 64 + lane) * 8, make_frag<T>(lo, hi));
+          }
+        }
+      }
+      lds_barrier();   // MID: Delta and K^T fragments are in LDS; state fragments consumed
+      if constexpr (CH) {
+        // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
+        if constexpr (!TRK) {   // K^T fragments built by the output waves before MID
+#pragma unroll
+          for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
+          gl = GT[192];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Each tile is scaled by gamma_last right before its first product, and the
+        // next chunk's state fragments of a tile pair (kept for the chain's K*S,
+        // stored for the output wave) are formed two products after the pair's
+        // last one, so VALU work overlaps the matrix products.
+        constexpr int U0 = (NKB2 - 1) * NST;   // first product of the last token block
+        auto next_sb = [&](int rt) {
+          if (rt >= 0 && (rt % 2 == 1 || rt == NST - 1)) {
+            const int kb = rt / 2;
+            Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
+            store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
+          }
+        };
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          if (u < NST) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) S[u][q] *= gl;
+          }
+          mma<T>(S[u % NST], kt[u], u / NST == 0 ? Tb0 : Tb1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (u + LA < NU) kt[u + LA] = kt_frag((u + LA) % NST, (u + LA) / NST);
+          if (u - 2 >= U0) next_sb(u - 2 - U0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        next_sb(NST - 2);
+        next_sb(NST - 1);
+        if constexpr (EMIT) {
+          // the state after this chunk's last token, in the [dk, dv] state layout:
+          // a wave-uniform row base per store plus one per-lane 32-bit offset
+          if (active && (int64_t)(cbeg + c) < p.chunk_states_cap) {
+            float* cs = p.chunk_states + ((size_t)(cbeg + c) * p.Hv + h) * DK * dv;
+            const int lo = (DK < 32 ? 4 * g4 : 8 * g4) * dv + col0 + i16;
+#pragma unroll
+            for (int r = 0; r < NST; ++r)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int row = perm_dk<DK>(16 * r + q);          // lane group 0's row
+                (cs + (size_t)row * dv)[lo] = S[r][q];
+              }
+          }
+        }
+      } else {
+        // ---- O = scale (gamma QS + MP Delta) -> o -----------------------------------
+        const Frag<T> Db0 = load_frag_native<T>(dx_mine), Db1 = load_frag_native<T>(dx_mine + 512);
+        f32x4 O[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 128 + 16 * r + 4 * g4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) O[r][q] = gm[q] * QSa[r][q];
+          if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 0)) * 64 + lane) * 8), Db0);
+        }
+#pragma unroll
+        for (int r = 2; r < nrt; ++r)
+          mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 1)) * 64 + lane) * 8), Db1);
+        if (active) {
+          T* oc = op + (size_t)t0 * ostride + olane;
+          if (len == C) {
+#pragma unroll
+            for (int r = 0; r < nrt; ++r)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              plo[j] = (4 * g4 + j == i16) ? 1.f : 0.f;
-              phi[j] = 0.f;
-            }
+            for (int r = 0; r < nrt; ++r)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (16 * r + 4 * g4 + q < len) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
           }
-          const Frag<T> pf = make_frag<T>(plo, phi);
-          f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-          if (2 * kb < nrt) mma<T>(lo, kq_frag(Kt, 32 * kb + i16, rt >> 1), pf);
-          if (2 * kb + 1 < nrt) mma<T>(hi, kq_frag(Kt, 32 * kb + 16 + i16, rt >> 1), pf);
-          store_frag_native<T>(KT + (f * 64 + lane) * 8, make_frag<T>(lo, hi));
         }
+      }
+      if constexpr (SM::NBUF == 1) {
+        // single stage buffer: chunk c+1 may only overwrite it once every wave is
+        // done reading chunk c (gamma, tail and MP are read after MID)
+        lds_barrier();
+        if (NDW == 0 && CH && c + 1 < nch) issue(c + 1, 0, 0);
       }
     }
-    lds_barrier();   // MID: Delta and K^T fragments are in LDS; state fragments consumed
-    if (chain) {
-      // ---- S = gamma_last S + K^T (tail * Delta) ---------------------------------
-      if constexpr (!TRK) {   // K^T fragments built by the output waves before MID
-#pragma unroll
-        for (int u = 0; u < NU && u < LA; ++u) kt[u] = kt_frag(u % NST, u / NST);
-        gl = GT[192];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // Each tile is scaled by gamma_last right before its first product, and the
-      // next chunk's state fragments of a tile pair (kept for the chain's K*S,
-      // stored for the output wave) are formed two products after the pair's
-      // last one, so VALU work overlaps the matrix products.
-      constexpr int U0 = (NKB2 - 1) * NST;   // first product of the last token block
-      auto next_sb = [&](int rt) {
-        if (rt >= 0 && (rt % 2 == 1 || rt == NST - 1)) {
-          const int kb = rt / 2;
-          Sb[kb] = make_frag<T>(S[2 * kb], 2 * kb + 1 < NST ? S[(2 * kb + 1) % NST] : f32x4{0.f, 0.f, 0.f, 0.f});
-          store_frag_native<T>(sx_mine + kb * 512, Sb[kb]);
-        }
-      };
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if (u < NST) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) S[u][q] *= gl;
-        }
-        mma<T>(S[u % NST], kt[u], u / NST == 0 ? Tb0 : Tb1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (u + LA < NU) kt[u + LA] = kt_frag((u + LA) % NST, (u + LA) / NST);
-        if (u - 2 >= U0) next_sb(u - 2 - U0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      next_sb(NST - 2);
-      next_sb(NST - 1);
-      if constexpr (EMIT) {
-        // the state after this chunk's last token, in the [dk, dv] state layout:
-        // a wave-uniform row base per store plus one per-lane 32-bit offset
-        if (active && (int64_t)(cbeg + c) < p.chunk_states_cap) {
-          float* cs = p.chunk_states + ((size_t)(cbeg + c) * p.Hv + h) * DK * dv;
-          const int lo = (DK < 32 ? 4 * g4 : 8 * g4) * dv + col0 + i16;
-#pragma unroll
-          for (int r = 0; r < NST; ++r)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int row = perm_dk<DK>(16 * r + q);          // lane group 0's row
-              (cs + (size_t)row * dv)[lo] = S[r][q];
-            }
-        }
-      }
-    } else if (!dmaw) {
-      // ---- O = scale (gamma QS + MP Delta) -> o -----------------------------------
-      const Frag<T> Db0 = load_frag_native<T>(dx_mine), Db1 = load_frag_native<T>(dx_mine + 512);
-      f32x4 O[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(GT + 128 + 16 * r + 4 * g4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) O[r][q] = gm[q] * QSa[r][q];
-        if (r < nrt) mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 0)) * 64 + lane) * 8), Db0);
-      }
-#pragma unroll
-      for (int r = 2; r < nrt; ++r)
-        mma<T>(O[r], load_frag_native<T>(AMP + ((NTRI + tri_idx(r, 1)) * 64 + lane) * 8), Db1);
-      if (active) {
-        T* oc = op + (size_t)t0 * ostride + olane;
-        if (len == C) {
-#pragma unroll
-          for (int r = 0; r < nrt; ++r)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < nrt; ++r)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (16 * r + 4 * g4 + q < len) oc[(size_t)(16 * r + q) * ostride] = Elem<T>::from_f(p.scale * O[r][q]);
-        }
-      }
-    }
-    if constexpr (SM::NBUF == 1) {
-      // single stage buffer: chunk c+1 may only overwrite it once every wave is
-      // done reading chunk c (gamma, tail and MP are read after MID)
-      lds_barrier();
-      if (NDW == 0 && issuer && c + 1 < nch) issue(c + 1, 0, 0);
-    }
-  }
+
+  };
+  if (chain) chunk_loop(std::true_type{});
+  else chunk_loop(std::false_type{});
 
   if (chain && p.s_out != nullptr && active) {
     float* so = p.s_out + ((size_t)s * p.Hv + h) * DK * dv + col0 + i16;
