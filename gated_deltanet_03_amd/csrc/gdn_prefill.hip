@@ -665,7 +665,11 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   constexpr int nrt = C / 16;
   constexpr int NST = SM::NST, NSB = SM::NSB, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
   constexpr int RPI_K = 64 / PPR;         // K rows per DMA instruction
-  constexpr int NA = SM::AB / 1024;       // DMA instructions for A' and MP
+  constexpr int NA = SM::AB / 1024;       // 1 KB pieces of the A' and MP region
+  // 16-bit inputs: the chain fetches A' into its registers and only MP is
+  // staged (fp32 A' fragments are too wide for the chain's registers)
+  constexpr bool AREG = ES == 2;
+  constexpr int NA0 = AREG ? NA / 2 : 0;  // first staged piece of the A'/MP region
   extern __shared__ __align__(16) unsigned char smem_raw[];
   unsigned char* fixed = smem_raw + SM::NBUF * SM::STAGE;
   T* KT = reinterpret_cast<T*>(fixed);
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   // ---- DMA slots of chain wave wq (compile-time counts, loop-invariant 32-bit
   //      byte offsets from the chunk's wave-uniform base pointers, so each DMA
   //      is one scalar-base + vector-offset load) -------------------------------
-  constexpr int KPW = (PPR + NG - 1) / NG, VPW = (SW / PER + NG - 1) / NG, APW = (NA + NG - 1) / NG;
+  constexpr int KPW = (PPR + NG - 1) / NG, VPW = (SW / PER + NG - 1) / NG, APW = (NA - NA0 + NG - 1) / NG;
   int krow[KPW], vrow[VPW];
   uint32_t kvo[KPW], vvo[VPW];
 #pragma unroll
@@ -753,7 +757,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     for (int w = 0; w < NG; ++w) {
       int n = 0;
       for (int m = 0; m < KPW; ++m) n += (w + NG * m < PPR) ? 2 : 0;
-      for (int m = 0; m < APW; ++m) n += (w + NG * m < NA) ? 1 : 0;
+      for (int m = 0; m < APW; ++m) n += (NA0 + w + NG * m < NA) ? 1 : 0;
       mn = n < mn ? n : mn;
     }
     return mn;
@@ -804,7 +808,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     const char* ab = reinterpret_cast<const char*>(blk.A);
 #pragma unroll
     for (int m = 0; m < APW && part != 1; ++m) {
-      const int j = wq + NG * m;
+      const int j = NA0 + wq + NG * m;
       if (j < NA) dma16(ab + (uint32_t)((j * 64 + lane) * 16), sb + SM::OA + j * 1024);
     }
     if (part != 1 && wq == NG - 1) dma16(reinterpret_cast<const char*>(blk.gk) + 16 * lane, sb + SM::OG);
@@ -925,6 +929,18 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   // same barriers.
   auto chunk_loop = [&](auto role) {
     constexpr bool CH = decltype(role)::value;
+    // chain: the A' fragments of chunk c+1 are fetched from the workspace into
+    // registers while chunk c computes (they are the chain's alone, so they skip
+    // the LDS stage)
+    Frag<T> a_nx[AREG ? NTRI : 1];
+    auto fetch_a = [&](int cc) {
+      if constexpr (AREG) {
+        const Block<T> blk(p.chunk_data, (size_t)(cbeg + cc), p.Hv, h);
+#pragma unroll
+        for (int f = 0; f < NTRI; ++f) a_nx[f] = load_frag_native<T>(blk.A + (f * 64 + lane) * 8);
+      }
+    };
+    if (CH && nch > 0) fetch_a(0);
     for (int c = 0; c < nch; ++c) {
       const int buf = SM::NBUF == 3 ? c % 3 : (SM::NBUF == 2 ? (c & 1) : 0);
       const int t0 = st0 + c * C;
@@ -968,10 +984,15 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
       if constexpr (CH) {
         // ---- LDS reads and products in a fixed interleave: at most ~14 reads in
         //      flight (the LDS counter a wait can name stops at 15), K blocks two
-        //      ahead of the products that use them, and gamma, A' and tail
+        //      ahead of the products that use them, and gamma (A' for fp32) and tail
         //      prefetched behind the last K block ----------------------------------
-        constexpr int X1 = NSB >= 2 ? NSB - 2 : 0;   // step that prefetches gamma and A'
+        constexpr int X1 = NSB >= 2 ? NSB - 2 : 0;   // step that prefetches gamma (and fp32 A')
         Frag<T> ak[NSB][nrt], av[nrt], aa[NTRI];
+        if constexpr (AREG) {
+#pragma unroll
+          for (int f = 0; f < NTRI; ++f) aa[f] = a_nx[f];
+          if (c + 1 < nch) fetch_a(c + 1);
+        }
         f32x4 gm[4], tl[4];
         auto load_kblock = [&](int kb) {
 #pragma unroll
@@ -1000,10 +1021,12 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
           if (kb == X1) {
 #pragma unroll
             for (int r = 0; r < nrt; ++r) gm[r] = *reinterpret_cast<const f32x4*>(GT + 16 * r + 4 * g4);
+            if constexpr (!AREG) {
 #pragma unroll
-            for (int r = 0; r < nrt; ++r) aa[tri_idx(r, 0)] = load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8);
+              for (int r = 0; r < nrt; ++r) aa[tri_idx(r, 0)] = load_frag_native<T>(AMP + (tri_idx(r, 0) * 64 + lane) * 8);
 #pragma unroll
-            for (int r = 2; r < nrt; ++r) aa[tri_idx(r, 1)] = load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8);
+              for (int r = 2; r < nrt; ++r) aa[tri_idx(r, 1)] = load_frag_native<T>(AMP + (tri_idx(r, 1) * 64 + lane) * 8);
+            }
           }
           if (kb == NSB - 1) {
 #pragma unroll
