@@ -666,9 +666,11 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   constexpr int NST = SM::NST, NSB = SM::NSB, PER = SM::PER, PPR = SM::PPR, ES = SM::ES;
   constexpr int RPI_K = 64 / PPR;         // K rows per DMA instruction
   constexpr int NA = SM::AB / 1024;       // 1 KB pieces of the A' and MP region
-  // 16-bit inputs: the chain fetches A' into its registers and only MP is
-  // staged (fp32 A' fragments are too wide for the chain's registers)
-  constexpr bool AREG = ES == 2;
+  // 16-bit inputs with dedicated loaders: the chain fetches A' into its
+  // registers and only MP is staged (fp32 A' fragments are too wide for the
+  // chain's registers; where the chain waves issue the loads themselves the
+  // staged form measured faster)
+  constexpr bool AREG = ES == 2 && NDW > 0;
   constexpr int NA0 = AREG ? NA / 2 : 0;  // first staged piece of the A'/MP region
   extern __shared__ __align__(16) unsigned char smem_raw[];
   unsigned char* fixed = smem_raw + SM::NBUF * SM::STAGE;
