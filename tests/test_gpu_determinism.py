@@ -43,8 +43,14 @@ def test_repeated_calls_are_bitwise_identical(gdn):
     args = [dec[x] for x in ("q", "k", "v", "g", "beta")]
     kw = dict(scale=dec["scale"], initial_state=dec["s0"], cu_seqlens=dec["cu_seqlens"], state_update_capacity=7,
               capture_count=dec["capture_count"], state_update_active=1)
-    a = gdn.gdn_recurrent_step(*args, **kw)
-    b = gdn.gdn_recurrent_step(*args, **kw)
+    # zero-filled record buffers: slots past a row's captured prefix are never
+    # written, so they must still be zero in both (a fresh torch.empty buffer
+    # would hold whatever the allocator left there)
+    R = dec["Hv"] + dec["Hq"] * dec["dk"] + dec["Hv"] * dec["dv"]
+    su_a = torch.zeros((dec["num_seqs"], 7, R), device=dec["s0"].device)
+    su_b = torch.zeros_like(su_a)
+    a = gdn.gdn_recurrent_step(*args, state_update=su_a, **kw)
+    b = gdn.gdn_recurrent_step(*args, state_update=su_b, **kw)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
