@@ -556,10 +556,11 @@ __global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) voi
 
 // ---------------------------------------------------------------------------
 // 3. state pass: one workgroup per (sequence, value head, slice of 16*NG columns),
-//    2*NG waves (NG = 2 or 4 column groups of 16).
+//    2*NG compute waves (NG = 2 or 4 column groups of 16) plus NDW load-issuing
+//    waves.
 //
-//    Each 16-column group of the slice is served by two waves that share a
-//    SIMD: a chain wave (waves 0..NG-1) owning the fp32 state of those columns and
+//    Each 16-column group of the slice is served by two waves: a chain wave
+//    (waves 0..NG-1) owning the fp32 state of those columns and
 //    running the sequential part, K*S -> X -> A'*X -> S update; and an output
 //    wave (waves NG..2NG-1) running everything off that path: Q*S, the K^T fragments,
 //    MP*Delta and the o stores.  The state crosses over as bf16/f16 fragments
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   const bool issuer = NDW > 0 ? dmaw : chain;
   const int wq = wave & (NG - 1);                               // column group (load slot for loaders)
   // the chain waves carry the sequential dependence: let them win instruction
-  // arbitration against the output wave that shares their SIMD
+  // arbitration against any wave that shares their SIMD
   if (chain) __builtin_amdgcn_s_setprio(2);
   const int ncols = min(SW, p.dv - SW * slice);
   const int col0 = SW * slice + 16 * wq;
