@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(PrefillArgs p) {
     scan[threadIdx.x] = n;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
-      int v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      int v = (int)threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
       __syncthreads();
       scan[threadIdx.x] += v;
       __syncthreads();
@@ -767,9 +767,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   }();
   static_assert(LB >= 0 && LB <= 63, "vmcnt immediate");
   const int kq_row_stride = p.Hq * DK, v_row_stride = p.Hv * dv;
-  // part 0: every load of chunk c; 1: the K and Q tiles; 2: V, A'/MP and the
-  // factor vector
-  auto issue = [&](int c, int buf, int part) {
+  auto issue = [&](int c, int buf) {
     const int t0 = st0 + c * C;
     const int last = min(C, st1 - t0) - 1;
     unsigned char* sb = smem_raw + buf * SM::STAGE;
@@ -779,7 +777,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     Block<T> blk(p.chunk_data, (size_t)(cbeg + c), p.Hv, h);
     if (last == C - 1) {   // full chunk: no row needs clamping
 #pragma unroll
-      for (int m = 0; m < KPW && part != 2; ++m) {
+      for (int m = 0; m < KPW; ++m) {
         const int j = wq + NG * m;
         if (j < PPR) {
           dma16(kc + kvo[m], sb + SM::OK_ + j * 1024);
@@ -787,13 +785,13 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         }
       }
 #pragma unroll
-      for (int m = 0; m < VPW && part != 1; ++m) {
+      for (int m = 0; m < VPW; ++m) {
         const int j = wq + NG * m;
         if (j < pprv) dma16(vc + vvo[m], sb + SM::OV + j * 1024);
       }
     } else {               // last chunk of a sequence: rows past its end repeat its last row
 #pragma unroll
-      for (int m = 0; m < KPW && part != 2; ++m) {
+      for (int m = 0; m < KPW; ++m) {
         const int j = wq + NG * m;
         if (j < PPR) {
           const int64_t d = (int64_t)(min(krow[m], last) - krow[m]) * kq_row_stride * ES;
@@ -802,7 +800,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         }
       }
 #pragma unroll
-      for (int m = 0; m < VPW && part != 1; ++m) {
+      for (int m = 0; m < VPW; ++m) {
         const int j = wq + NG * m;
         if (j < pprv) dma16(vc + vvo[m] + (int64_t)(min(vrow[m], last) - vrow[m]) * v_row_stride * ES,
                             sb + SM::OV + j * 1024);
@@ -810,11 +808,11 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     }
     const char* ab = reinterpret_cast<const char*>(blk.A);
 #pragma unroll
-    for (int m = 0; m < APW && part != 1; ++m) {
+    for (int m = 0; m < APW; ++m) {
       const int j = NA0 + wq + NG * m;
       if (j < NA) dma16(ab + (uint32_t)((j * 64 + lane) * 16), sb + SM::OA + j * 1024);
     }
-    if (part != 1 && wq == NG - 1) dma16(reinterpret_cast<const char*>(blk.gk) + 16 * lane, sb + SM::OG);
+    if (wq == NG - 1) dma16(reinterpret_cast<const char*>(blk.gk) + 16 * lane, sb + SM::OG);
   };
 
 
@@ -876,8 +874,8 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  if (issuer && nch > 0) issue(0, 0, 0);
-  if (SM::NBUF == 3 && issuer && nch > 1) issue(1, 1, 0);
+  if (issuer && nch > 0) issue(0, 0);
+  if (SM::NBUF == 3 && issuer && nch > 1) issue(1, 1);
   if constexpr (NDW > 0) {
     // Load-issuing waves run a loop of their own with the same workgroup
     // barriers per chunk as the compute waves (TOP, MID, and a third with a
@@ -889,11 +887,11 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         wait_chunk(c);
         lds_barrier();   // TOP
         const int cn = c + SM::NBUF - 1;
-        if (SM::NBUF >= 2 && cn < nch) issue(cn, SM::NBUF == 3 ? cn % 3 : (c & 1) ^ 1, 0);
+        if (SM::NBUF >= 2 && cn < nch) issue(cn, SM::NBUF == 3 ? cn % 3 : (c & 1) ^ 1);
         lds_barrier();   // MID
         if constexpr (SM::NBUF == 1) {
           lds_barrier();
-          if (c + 1 < nch) issue(c + 1, 0, 0);
+          if (c + 1 < nch) issue(c + 1, 0);
         }
       }
       return;
@@ -1006,7 +1004,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         for (int r = 0; r < nrt; ++r) av[r] = v_frag(Vs, 16 * r + i16);
         if constexpr (NSB > 1) load_kblock(1);
         __builtin_amdgcn_sched_barrier(0);
-        if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1, 0);
+        if (NDW == 0 && SM::NBUF == 2 && c + 1 < nch) issue(c + 1, buf ^ 1);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 KSa[4], Va[4];
 #pragma unroll
@@ -1206,7 +1204,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         // single stage buffer: chunk c+1 may only overwrite it once every wave is
         // done reading chunk c (gamma, tail and MP are read after MID)
         lds_barrier();
-        if (NDW == 0 && CH && c + 1 < nch) issue(c + 1, 0, 0);
+        if (NDW == 0 && CH && c + 1 < nch) issue(c + 1, 0);
       }
     }
 
