@@ -142,6 +142,46 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _expect(t, name, numel, at_least=False):
+    """Raise ValueError unless tensor t holds exactly (or at least) numel elements.
+    The C ABI sees bare pointers, so sizes are checked here, before any call."""
+    if t is None:
+        return
+    n = t.numel()
+    if (n < numel) if at_least else (n != numel):
+        rel = "at least " if at_least else ""
+        raise ValueError(f"{name} has {n} elements, expected {rel}{numel}")
+
+
+def _check_tokens(sh, q, k, v, g, beta, o, cu_seqlens):
+    """Token tensors against the problem description built from q and v."""
+    ntok = sh.T if cu_seqlens is not None else sh.B * sh.T
+    if tuple(k.shape) != tuple(q.shape):
+        raise ValueError(f"k has shape {tuple(k.shape)}, q has {tuple(q.shape)}")
+    if v.dim() != q.dim() or tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
+        raise ValueError(f"v has shape {tuple(v.shape)}; its leading dims must match q's {tuple(q.shape[:-2])}")
+    _expect(v, "v", ntok * sh.Hv * sh.dv)
+    for t, n in ((g, "g"), (beta, "beta")):
+        if tuple(t.shape) != tuple(v.shape[:-1]):
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(v.shape[:-1])}")
+    if o is not None and tuple(o.shape) != tuple(v.shape):
+        raise ValueError(f"o has shape {tuple(o.shape)}, expected {tuple(v.shape)}")
+    if cu_seqlens is not None and cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be 1-D [N+1]")
+
+
+def _check_states(sh, initial_state, stride, final_state):
+    """initial_state covers (B-1)*stride + Hv*dk*dv elements; final_state is [B, Hv, dk, dv]."""
+    per = sh.Hv * sh.dk * sh.dv
+    if stride < 0:
+        raise ValueError(f"initial_state_batch_stride={stride} < 0")
+    if initial_state is not None and sh.B > 0:
+        _expect(initial_state, "initial_state", (sh.B - 1) * stride + per, at_least=True)
+    if final_state is not None and tuple(final_state.shape) != (sh.B, sh.Hv, sh.dk, sh.dv):
+        raise ValueError(f"final_state has shape {tuple(final_state.shape)}, expected "
+                         f"{(sh.B, sh.Hv, sh.dk, sh.dv)}")
+
+
 def _shape_from(q, k, v, scale, cu_seqlens):
     if cu_seqlens is None:
         if q.dim() != 4:
@@ -224,9 +264,12 @@ def _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride,
     if initial_state_batch_stride is None:
         initial_state_batch_stride = 0 if (initial_state is not None and initial_state.shape[0] == 1
                                            and sh.B > 1) else per
+    _check_tokens(sh, q, k, v, g, beta, o, cu_seqlens)
+    _check_states(sh, initial_state, int(initial_state_batch_stride), final_state)
     need = gdn_prefill_workspace_bytes(sh, chunk_size, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, dev)
     common = (ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
               int(initial_state_batch_stride), _ptr(cu_seqlens), int(chunk_size), _ptr(o), _ptr(final_state))
     if prologue is not None:
@@ -251,6 +294,9 @@ def _chunk_buffer(sh, cu_seqlens, chunk_size, chunk_states, num_chunks, dev):
     """(chunk_states view, buffer with an address) for the boundary states."""
     if chunk_states is not None:
         _need(chunk_states, "chunk_states", torch.float32, dev)
+        if chunk_states.dim() != 4 or tuple(chunk_states.shape[1:]) != (sh.Hv, sh.dk, sh.dv):
+            raise ValueError(f"chunk_states has shape {tuple(chunk_states.shape)}, expected "
+                             f"[num_chunks, {sh.Hv}, {sh.dk}, {sh.dv}]")
         return chunk_states, chunk_states
     if num_chunks is None:
         if cu_seqlens is None:
@@ -299,6 +345,16 @@ def gdn_recurrent_step(q, k, v, g, beta, *, scale=None, initial_state=None,
         R = sh.Hv + sh.Hq * sh.dk + sh.Hv * sh.dv
         state_update = torch.empty((sh.B, cap, R), dtype=torch.float32, device=dev)
     _need(state_update, "state_update", torch.float32, dev)
+    _check_tokens(sh, q, k, v, g, beta, o, cu_seqlens)
+    _check_states(sh, initial_state, int(initial_state_batch_stride), final_state)
+    if cap < 0:
+        raise ValueError(f"state_update_capacity={cap} < 0")
+    if cap > 0:
+        if capture_count is None:
+            raise ValueError("capture_count is required when state_update_capacity > 0")
+        _expect(capture_count, "capture_count", sh.B, at_least=True)
+        R = sh.Hv + sh.Hq * sh.dk + sh.Hv * sh.dv
+        _expect(state_update, "state_update", sh.B * cap * R, at_least=True)
     rest = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), int(initial_state_batch_stride),
             _ptr(cu_seqlens), _ptr(o), _ptr(final_state), cap, _ptr(capture_count), int(state_update_active),
             _ptr(state_update), _stream(dev))
@@ -319,6 +375,19 @@ def gdn_replay_state_updates(state, state_update, replay_count, *, Hq, state_upd
     _need(state, "state", torch.float32, dev)
     _need(state_update, "state_update", torch.float32, dev)
     _need(replay_count, "replay_count", torch.int32, dev)
+    if state.dim() != 4:
+        raise ValueError(f"state must be [B, Hv, dk, dv], got shape {tuple(state.shape)}")
+    Hq = int(Hq)
+    if Hq <= 0 or Hv % Hq != 0:
+        raise ValueError(f"Hq={Hq} must be positive and divide Hv={Hv}")
+    if cap < 0:
+        raise ValueError(f"state_update_capacity={cap} < 0")
+    R = Hv + Hq * dk + Hv * dv
+    if state_update.dim() == 3 and state_update.shape[-1] != R:
+        raise ValueError(f"state_update records hold {state_update.shape[-1]} floats; Hv + Hq*dk + Hv*dv = {R}")
+    if cap > 0:
+        _expect(state_update, "state_update", B * cap * R, at_least=True)
+        _expect(replay_count, "replay_count", B, at_least=True)
     _check(lib.gdn_replay_state_updates(B, int(Hq), Hv, dk, dv, cap, _ptr(state_update), _ptr(replay_count),
                                         _ptr(state), _stream(dev)))
     return state
@@ -332,6 +401,10 @@ def gdn_state_snapshot(src, dst=None):
     if dst is None:
         dst = torch.empty_like(src)
     _need(dst, "dst", torch.float32, dev)
+    if src.dim() != 4:
+        raise ValueError(f"src must be [N, Hv, dk, dv], got shape {tuple(src.shape)}")
+    if tuple(dst.shape) != tuple(src.shape):
+        raise ValueError(f"dst has shape {tuple(dst.shape)}, src {tuple(src.shape)}")
     N, Hv, dk, dv = src.shape
     _check(lib.gdn_state_snapshot(_ptr(src), _ptr(dst), N, Hv, dk, dv, _stream(dev)))
     return dst

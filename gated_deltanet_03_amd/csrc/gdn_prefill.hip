@@ -32,6 +32,7 @@
 //
 // A' and MP are written in fragment-native order (gdn_mfma.h), lower-triangular
 // 16x32 blocks only: block (r, kb) with kb <= r/2, i.e. 6 blocks per matrix.
+#include <atomic>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -1224,16 +1225,33 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
+// Per-device host caches are atomics: entry points may be called from several
+// host threads, each on any device.
+constexpr int kMaxDevices = 64;
+
 static int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
+}
+
+// The dynamic-LDS limit of a kernel is a per-device attribute: set it once per
+// device on first use.  Setting it is idempotent, so two threads racing on the
+// first call of a device both succeed; the flag only skips later calls.
+static hipError_t ensure_dynamic_lds(std::atomic<bool>* done, const void* fn, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
+  return e;
 }
 
 template <typename T, int DK, int C, int NG, int NDW, bool EMIT>
@@ -1241,13 +1259,9 @@ static hipError_t launch_state(const PrefillArgs& a, hipStream_t st) {
   using SM = StateSmem<T, DK, NG, sizeof(T) == 2 && DK == 128 && C >= 32, (NDW > 0 && !EMIT)>;
   const size_t sm2 = SM::total;
   if (sm2 > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)chunk_state_kernel<T, DK, C, NG, NDW, EMIT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<bool> attr_set[kMaxDevices];
+  const hipError_t ea = ensure_dynamic_lds(attr_set, (const void*)chunk_state_kernel<T, DK, C, NG, NDW, EMIT>, sm2);
+  if (ea != hipSuccess) return ea;
   const int nslices = (a.dv + SM::SW - 1) / SM::SW;
   const long long groups = (long long)a.Hq * a.B;
   const long long sblocks = 8LL * nslices * (a.Hv / a.Hq) * ((groups + 7) / 8);

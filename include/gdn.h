@@ -129,6 +129,15 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape* shape, int32_t chunk_size, i
  * partial).  The result equals the token-by-token recurrence up to rounding.
  * fp32 inputs are supported for dk <= 64 (GDN_ERR_UNSUPPORTED above).
  *
+ * Precondition on g: every g <= 0 (decay alpha = exp(g) <= 1), the usual case
+ * of a forgetting gate.  The chunked form then only forms decay ratios
+ * exp(G_i - G_j) with j <= i, exp(G_i) and exp(G_last - G_j) (G = in-chunk
+ * cumulative sum of g), all <= 1, which keeps its 16-bit matrix operands in
+ * range.  With some g > 0 those factors exceed 1 and can overflow 16-bit
+ * operands, so o and final_state are unspecified (the call still completes
+ * and accesses only the buffers given).  The precondition is not checked (g is
+ * not read on the host); gdn_recurrent_step accepts any finite g.
+ *
  *  initial_state   [N, Hv, dk, dv] fp32 or NULL (zeros).  Sequence s reads
  *                  initial_state + s * initial_state_batch_stride (elements);
  *                  stride 0 broadcasts one state to all sequences (snapshot

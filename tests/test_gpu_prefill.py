@@ -10,7 +10,7 @@ import torch
 
 import gdn_inputs as gi
 import oracle
-from gpu_common import DEV, assert_close, say, sha, to_dev
+from gpu_common import DEV, assert_close, case_bounds, say, sha, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def test_prefill_qwen_fp16(gdn):
     say(f"case qwen_fp16 T=2048 Hq=2 Hv=6 seed={case['seed']}")
     o, fin = prefill(gdn, case, case["chunk"])
     ref = oracle_run(case)
-    assert_close(o, ref["o"], "f16", "o")
+    assert_close(o, ref["o"], "f16", "o", bounds=case_bounds(case), chunk=case["chunk"])
     assert_close(fin, ref["final"], "f16", "final")
 
 
@@ -73,10 +73,8 @@ def test_prefill_long_varlen_sampled_heads(gdn):
     o, fin = prefill(gdn, case, case["chunk"])
     heads = [0, 17, 31]   # key heads 0 and 8 (two value heads of key head 0 differ by decay only)
     ref = oracle_run(case, heads=heads)
-    for h in heads:
-        for s, (t0, t1) in enumerate(oracle.sequence_bounds(0, 0, case["cu_seqlens"].numpy())):
-            assert_close(o[t0:t1, h], ref["o"][t0:t1, h], "bf16", f"o seq {s} head {h}")
-            assert_close(fin[s, h], ref["final"][s, h], "bf16", f"final seq {s} head {h}")
+    assert_close(o, ref["o"], "bf16", "o", bounds=case_bounds(case), chunk=case["chunk"], heads=heads)
+    assert_close(fin, ref["final"], "bf16", "final", heads=heads)
     assert torch.isfinite(o).all() and torch.isfinite(fin).all()
 
 
@@ -88,9 +86,23 @@ def test_prefill_ragged_chunk_boundaries(gdn, chunk, dtype):
     say(f"case ragged {dtype} chunk={chunk} lengths={lengths}")
     o, fin = prefill(gdn, case, chunk)
     ref = oracle_run(case)
-    assert_close(o, ref["o"], dtype, "o")
+    assert_close(o, ref["o"], dtype, "o", bounds=case_bounds(case), chunk=chunk)
     assert_close(fin, ref["final"], dtype, "final")
     assert torch.equal(fin[0].cpu(), case["s0"][0])        # empty sequence: final = initial
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_ragged_dk128_short_and_partial_chunks(gdn, chunk, dtype):
+    """16-bit inputs at dk = dv = 128 and C >= 32 take the transpose-read K^T
+    path; short sequences and partial last chunks are checked one by one."""
+    lengths = [1, 15, 16, 17, 31, 33, 63, 65, 200]
+    case = gi.random_case(520 + chunk, lengths, Hq=2, Hv=4, dk=128, dv=128, dtype=dtype)
+    say(f"case ragged dk128 {dtype} chunk={chunk} lengths={lengths}")
+    o, fin = prefill(gdn, case, chunk)
+    ref = oracle_run(case)
+    assert_close(o, ref["o"], dtype, "o", bounds=case_bounds(case), chunk=chunk)
+    assert_close(fin, ref["final"], dtype, "final")
 
 
 @pytest.mark.parametrize("dk,dv,Hq,Hv", [(16, 16, 1, 1), (32, 64, 2, 2), (128, 32, 1, 4), (64, 16, 3, 6)])
@@ -99,7 +111,7 @@ def test_prefill_head_dims(gdn, dk, dv, Hq, Hv):
     say(f"case head dims dk={dk} dv={dv} Hq={Hq} Hv={Hv}")
     o, fin = prefill(gdn, case, 64)
     ref = oracle_run(case)
-    assert_close(o, ref["o"], "bf16", "o")
+    assert_close(o, ref["o"], "bf16", "o", bounds=case_bounds(case), chunk=64)
     assert_close(fin, ref["final"], "bf16", "final")
 
 
@@ -108,7 +120,7 @@ def test_prefill_chunk_size_does_not_change_results(gdn):
     say("case chunk-size independence")
     outs = [prefill(gdn, case, c) for c in (16, 32, 64)]
     for o, fin in outs[1:]:
-        assert_close(o, outs[0][0], "bf16", "o across chunk sizes")
+        assert_close(o, outs[0][0], "bf16", "o across chunk sizes", bounds=case_bounds(case))
         assert_close(fin, outs[0][1], "bf16", "final across chunk sizes")
 
 
@@ -124,7 +136,7 @@ def test_prefill_split_sequence_carries_state(gdn):
                   beta=case["beta"][m:], cu_seqlens=torch.tensor([0, 300 - m], dtype=torch.int32), T=300 - m)
     o1, f1 = prefill(gdn, first, 64)
     o2, f2 = prefill(gdn, second, 64, initial_state=f1)
-    assert_close(torch.cat([o1, o2]), o_all, "bf16", "o split vs whole")
+    assert_close(torch.cat([o1, o2]), o_all, "bf16", "o split vs whole", bounds=[(0, m), (m, 300)])
     assert_close(f2, fin_all, "bf16", "final split vs whole")
 
 
@@ -159,8 +171,7 @@ def test_prefix_snapshot_reuse(gdn):
         if bi in checked:
             say(f"oracle check batch {bi}")
             ref = oracle_run(bt, heads=heads, s0=pref["final"][:1], broadcast=True)
-            for h in heads:
-                assert_close(o[:, h], ref["o"][:, h], "bf16", f"batch {bi} head {h}")
+            assert_close(o, ref["o"], "bf16", f"batch {bi} o", bounds=case_bounds(bt), chunk=64, heads=heads)
 
 
 @pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f16", 32)])
@@ -177,7 +188,7 @@ def test_prefill_many_rows_geometry(gdn, dtype, C):
     torch.cuda.synchronize()
     ref = oracle.recurrent(case["q"], case["k"], case["v"], case["g"], case["beta"], case["scale"], 2, 4,
                            cu_seqlens=case["cu_seqlens"], initial_state=case["s0"], boundary_every=C)
-    assert_close(o, ref["o"], dtype, "o")
+    assert_close(o, ref["o"], dtype, "o", bounds=case_bounds(case), chunk=C)
     assert_close(fin, ref["final"], dtype, "final")
     assert_close(cs, ref["boundary"], dtype, "chunk states")
     o2, fin2 = gdn.gdn_prefill_chunked(*[d[x] for x in ("q", "k", "v", "g", "beta")], scale=case["scale"],
@@ -206,7 +217,7 @@ def test_prefill_many_sequences_plan(gdn, nseq):
     torch.cuda.synchronize()
     ref = oracle.recurrent(case["q"], case["k"], case["v"], case["g"], case["beta"], case["scale"], 1, 2,
                            cu_seqlens=case["cu_seqlens"], initial_state=case["s0"], boundary_every=C)
-    assert_close(o, ref["o"], "bf16", "o")
+    assert_close(o, ref["o"], "bf16", "o", bounds=case_bounds(case), chunk=C)
     assert_close(fin, ref["final"], "bf16", "final")
     assert_close(cs, ref["boundary"], "bf16", "chunk states")
     assert torch.equal(o, o2) and torch.equal(fin, fin2)
@@ -222,5 +233,5 @@ def test_prefill_many_dense_rows_plan(gdn):
     say(f"case dense B={B} T={T}")
     o, fin = prefill(gdn, case, 32)
     ref = oracle_run(case)
-    assert_close(o, ref["o"], "bf16", "o")
+    assert_close(o, ref["o"], "bf16", "o", bounds=case_bounds(case), chunk=32)
     assert_close(fin, ref["final"], "bf16", "final")
