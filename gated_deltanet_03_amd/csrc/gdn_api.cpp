@@ -181,9 +181,6 @@ static gdn_status prefill_impl(const gdn_shape* sh, const gdn_prologue* pro, con
   if ((st = check_prologue(pro, &pr)) != GDN_OK) return st;
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d: supported chunk sizes are 16, 32, 64", chunk);
-  if (sh->dtype == GDN_F32 && sh->dk > 64)
-    return fail(GDN_ERR_UNSUPPORTED, "fp32 chunked prefill supports dk <= 64 (LDS capacity); use fp16/bf16 or the "
-                                     "recurrent step");
   if ((st = check_tokens(sh, total, q, k, v, g, beta, o)) != GDN_OK) return st;
   if ((st = check_states(sh, s0, s0_stride, s_out)) != GDN_OK) return st;
   if (sh->B == 0) return GDN_OK;

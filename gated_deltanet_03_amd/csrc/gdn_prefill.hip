@@ -270,7 +270,7 @@ __device__ __forceinline__ void mma_tn(f32x4& acc, const f32x4& e, const f32x4& 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T, int DK, int C, int HPW>
-__global__ __launch_bounds__(64, (HPW == 1 && DK == 128 && C == 64) ? 2 : 3) void chunk_prep_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(64, (sizeof(T) == 4 && DK == 128) ? 1 : ((HPW == 1 && DK == 128 && C == 64) ? 2 : 3)) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int nrt = C / 16;
   constexpr int NKB = DK >= 32 ? DK / 32 : 1;
   constexpr float LOG2E = 1.4426950408889634f;
@@ -1307,7 +1307,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   // The chunk-boundary state stores live in a separate instantiation so that
   // the plain prefill keeps its register allocation.
   const bool emit = a.chunk_states != nullptr;
-  if ((long long)a.B * a.Hv * ((a.dv + 31) / 32) <= 2LL * device_cus())
+  // fp32 tiles at dk = 128 fit the LDS only in the 32-column geometry with one
+  // stage buffer; 4 waves (the chain waves issuing the loads), so each wave
+  // may hold the register budget of a whole SIMD and nothing spills
+  constexpr bool only32 = sizeof(T) == 4 && DK == 128;
+  if constexpr (only32)
+    e = emit ? launch_state<T, DK, C, 2, 0, true>(a, st) : launch_state<T, DK, C, 2, 0, false>(a, st);
+  else if ((long long)a.B * a.Hv * ((a.dv + 31) / 32) <= 2LL * device_cus())
     e = emit ? launch_state<T, DK, C, 2, 2, true>(a, st)    // 6 waves: + two load-issuing waves
              : launch_state<T, DK, C, 2, 2, false>(a, st);
   else
@@ -1333,10 +1339,7 @@ static hipError_t launch_prefill_dt(const PrefillArgs& a, hipStream_t st) {
     case 16: return launch_prefill_c<T, 16>(a, st);
     case 32: return launch_prefill_c<T, 32>(a, st);
     case 64: return launch_prefill_c<T, 64>(a, st);
-    case 128:
-      // fp32 with dk = 128 does not fit the state kernel's LDS budget (rejected on the host)
-      if constexpr (sizeof(T) == 4) return hipErrorInvalidValue;
-      else return launch_prefill_c<T, 128>(a, st);
+    case 128: return launch_prefill_c<T, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -127,7 +127,6 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape* shape, int32_t chunk_size, i
  * last token, processing each sequence in chunks of `chunk_size` tokens
  * (16, 32 or 64; chunks restart at each sequence start, the last one may be
  * partial).  The result equals the token-by-token recurrence up to rounding.
- * fp32 inputs are supported for dk <= 64 (GDN_ERR_UNSUPPORTED above).
  *
  * Precondition on g: every g <= 0 (decay alpha = exp(g) <= 1), the usual case
  * of a forgetting gate.  The chunked form then only forms decay ratios

@@ -105,6 +105,30 @@ def test_prefill_ragged_dk128_short_and_partial_chunks(gdn, chunk, dtype):
     assert_close(fin, ref["final"], dtype, "final")
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_prefill_fp32_dk128(gdn, chunk):
+    """The unquantised fp32 baseline at the Qwen-like head size dk = dv = 128:
+    ragged sequences (empty, single token, partial and exact chunks), random
+    initial states, final and chunk-boundary states, max-abs 1e-4."""
+    lengths = [0, 1, 17, 64, 65, 130]
+    case = gi.random_case(530 + chunk, lengths, Hq=2, Hv=4, dk=128, dv=128, dtype="f32")
+    say(f"case fp32 dk128 chunk={chunk} lengths={lengths}")
+    d = to_dev(case)
+    args = [d[x] for x in ("q", "k", "v", "g", "beta")]
+    o, fin, cs = gdn.gdn_prefill_chunked_states(*args, scale=case["scale"], cu_seqlens=d["cu_seqlens"],
+                                                chunk_size=chunk, initial_state=d["s0"])
+    o2, fin2 = gdn.gdn_prefill_chunked(*args, scale=case["scale"], cu_seqlens=d["cu_seqlens"], chunk_size=chunk,
+                                       initial_state=d["s0"])
+    torch.cuda.synchronize()
+    ref = oracle.recurrent(case["q"], case["k"], case["v"], case["g"], case["beta"], case["scale"], 2, 4,
+                           cu_seqlens=case["cu_seqlens"], initial_state=case["s0"], boundary_every=chunk)
+    assert_close(o, ref["o"], "f32", "o")
+    assert_close(fin, ref["final"], "f32", "final")
+    assert_close(cs, ref["boundary"], "f32", "chunk states")
+    assert torch.equal(o, o2) and torch.equal(fin, fin2)
+    assert torch.equal(fin[0].cpu(), case["s0"][0])
+
+
 @pytest.mark.parametrize("dk,dv,Hq,Hv", [(16, 16, 1, 1), (32, 64, 2, 2), (128, 32, 1, 4), (64, 16, 3, 6)])
 def test_prefill_head_dims(gdn, dk, dv, Hq, Hv):
     case = gi.random_case(600 + dk + dv, [70, 33], Hq=Hq, Hv=Hv, dk=dk, dv=dv, dtype="bf16")

@@ -69,7 +69,6 @@ def test_shape_validation(lib):
     assert step(lib, shape(B=-1)) == gdn.GDN_ERR_INVALID_ARG
     assert step(lib, shape(scale=float("nan"))) == gdn.GDN_ERR_INVALID_ARG
     assert prefill(lib, shape(), chunk=48) == gdn.GDN_ERR_UNSUPPORTED
-    assert prefill(lib, shape(dtype=gdn.GDN_F32, dk=128)) == gdn.GDN_ERR_UNSUPPORTED
 
 
 def test_pointer_validation(lib):
@@ -176,3 +175,4 @@ def test_status_strings(lib):
     for st in range(4):
         assert lib.gdn_status_string(st)
     assert b"unknown" in lib.gdn_status_string(99)
+
