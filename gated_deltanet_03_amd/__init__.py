@@ -30,7 +30,9 @@ _DTYPES = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_B
 EXPORTED = ("gdn_abi_version", "gdn_prefill_workspace_bytes", "gdn_prefill_chunked",
             "gdn_prefill_chunked_states", "gdn_prefill_chunked_ex", "gdn_recurrent_step",
             "gdn_recurrent_step_ex", "gdn_replay_state_updates", "gdn_state_snapshot",
-            "gdn_status_string", "gdn_last_error", "gdn_profile_enable", "gdn_profile_collect")
+            "gdn_status_string", "gdn_last_error", "gdn_profile_enable", "gdn_profile_collect",
+            "gdn_prefill_chunked_noalloc")
+GDN_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 
 class gdn_prologue(ctypes.Structure):
@@ -87,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_prefill_workspace_bytes.argtypes = [shp, i32, i32]
     lib.gdn_prefill_chunked.restype = i32
     lib.gdn_prefill_chunked.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]
+    lib.gdn_prefill_chunked_noalloc.restype = i32
+    lib.gdn_prefill_chunked_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp]
     lib.gdn_recurrent_step.restype = i32
     lib.gdn_prefill_chunked_states.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, i64, vp,
                                                sz, vp]
@@ -214,6 +218,41 @@ def gdn_prefill_chunked(q, k, v, g, beta, *, scale=None, initial_state=None,
     Returns (o, final_state or None)."""
     return _prefill(q, k, v, g, beta, scale, initial_state, initial_state_batch_stride, cu_seqlens,
                     chunk_size, o, final_state, output_final_state, workspace, False, None, None)[:2]
+
+
+def gdn_prefill_chunked_noalloc(q, k, v, g, beta, *, scale=None, initial_state=None,
+                                initial_state_batch_stride=None, cu_seqlens=None, chunk_size=64,
+                                o=None, final_state=None, output_final_state=True):
+    """gdn_prefill_chunked with the library's fixed device scratch array as the
+    workspace (the C entry point allocates nothing; pass ``o`` and
+    ``final_state`` to allocate nothing here either).  Returns (o, final_state
+    or None)."""
+    lib = load_library()
+    dev = q.device
+    sh = _shape_from(q, k, v, scale, cu_seqlens)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(initial_state, "initial_state", torch.float32, dev)
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, dev)
+    per = sh.Hv * sh.dk * sh.dv
+    if final_state is None and output_final_state:
+        final_state = torch.empty((sh.B, sh.Hv, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev)
+    if initial_state_batch_stride is None:
+        initial_state_batch_stride = 0 if (initial_state is not None and initial_state.shape[0] == 1
+                                           and sh.B > 1) else per
+    _check_tokens(sh, q, k, v, g, beta, o, cu_seqlens)
+    _check_states(sh, initial_state, int(initial_state_batch_stride), final_state)
+    _check(lib.gdn_prefill_chunked_noalloc(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                           _ptr(initial_state), int(initial_state_batch_stride),
+                                           _ptr(cu_seqlens), int(chunk_size), _ptr(o), _ptr(final_state),
+                                           _stream(dev)))
+    return o, final_state
 
 
 def gdn_prefill_chunked_states(q, k, v, g, beta, *, scale=None, initial_state=None,
@@ -428,5 +467,6 @@ def gdn_profile_collect() -> dict:
 
 __all__ = ["gdn_profile_enable", "gdn_profile_collect", "load_library", "GdnError", "gdn_shape",
            "gdn_prefill_workspace_bytes", "gdn_prefill_chunked", "gdn_prefill_chunked_states",
+           "gdn_prefill_chunked_noalloc", "GDN_NOALLOC_SCRATCH_BYTES",
            "gdn_prefill_chunked_ex", "gdn_recurrent_step_ex", "Prologue", "gdn_prologue",
            "gdn_recurrent_step", "gdn_replay_state_updates", "gdn_state_snapshot", "EXPORTED", "LIB_PATH"]

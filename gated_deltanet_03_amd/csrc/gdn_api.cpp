@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
@@ -263,6 +264,60 @@ gdn_status gdn_prefill_chunked_ex(const gdn_shape* sh, const gdn_prologue* pro, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Prefill without a caller workspace: the workspace lives in a fixed device
+// array of GDN_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the process
+// ends.  Its address on the current device is looked up once per device (the
+// first call made with that device current) with hipGetSymbolAddress; host
+// code only ever passes that address on, never the array's name.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+
+gdn_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(GDN_ERR_UNSUPPORTED, "device %d: the allocation-free prefill supports devices 0..%d", dev,
+                kScratchDevices - 1);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+  if (g_scratch_ptr[dev] == nullptr) return fail(GDN_ERR_HIP, "scratch array has no device address");
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+}  // namespace
+
+extern "C" gdn_status gdn_prefill_chunked_noalloc(const gdn_shape* sh, const void* q, const void* k, const void* v,
+                                                  const float* g, const float* beta, const float* s0,
+                                                  int64_t s0_stride, const int32_t* cu, int32_t chunk, void* o,
+                                                  float* s_out, void* stream) {
+  const size_t need = gdn_prefill_workspace_bytes(sh, chunk, cu != nullptr);
+  if (need == 0)   // invalid shape or chunk: let the common checks name the problem
+    return prefill_impl(sh, nullptr, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, nullptr, 0, nullptr, 0,
+                        stream, "gdn_prefill_chunked_noalloc launch");
+  if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "gdn_prefill_chunked_noalloc: this problem needs %zu bytes of workspace, above the fixed %zu-byte "
+                "scratch array; use gdn_prefill_chunked with a caller workspace",
+                need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  gdn_status st = scratch_on_current_device(&ws);
+  if (st != GDN_OK) return st;
+  return prefill_impl(sh, nullptr, q, k, v, g, beta, s0, s0_stride, cu, chunk, o, s_out, nullptr, 0, ws,
+                      (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream, "gdn_prefill_chunked_noalloc launch");
+}
 
 static gdn_status recurrent_impl(const gdn_shape* sh, const gdn_prologue* pro, const void* q, const void* k,
                                  const void* v, const float* g, const float* beta, const float* s0,

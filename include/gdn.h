@@ -197,6 +197,32 @@ gdn_status gdn_prefill_chunked_ex(const gdn_shape* shape, const gdn_prologue* pr
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The entry point itself allocates nothing:
+ * its workspace is a fixed device array of GDN_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held from the first call on that GPU until the process
+ * ends.  The caller still passes every input and output.
+ *
+ * Same arguments (minus workspace), layouts, results and errors as
+ * gdn_prefill_chunked, plus GDN_ERR_UNSUPPORTED when the problem needs more
+ * workspace than the array holds (gdn_prefill_workspace_bytes() >
+ * GDN_NOALLOC_SCRATCH_BYTES; at 16-bit inputs and chunk 64 that is about
+ * 10,000 (chunk, value head) pairs, e.g. 20,000 tokens at 32 value heads).
+ * The array keeps the last call's contents; every call writes each part of
+ * it that it reads, so nothing needs clearing.  All calls on one GPU share
+ * the array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give unspecified results, so order them on one stream.
+ * The first call on a device looks up the array's address (no allocation).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+gdn_status gdn_prefill_chunked_noalloc(const gdn_shape* shape, const void* q, const void* k,
+                                       const void* v, const float* g, const float* beta,
+                                       const float* initial_state, int64_t initial_state_batch_stride,
+                                       const int32_t* cu_seqlens, int32_t chunk_size, void* o,
+                                       float* final_state, void* stream);
+
+/*
  * Recurrent step with compact state-update capture [onnxruntime PR 32767,
  * "Changes": state_update_capacity, the required [batch] capture_count input,
  * the packed float32 state_update output, clamped per-row prefix capture,

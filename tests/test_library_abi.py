@@ -176,3 +176,14 @@ def test_status_strings(lib):
         assert lib.gdn_status_string(st)
     assert b"unknown" in lib.gdn_status_string(99)
 
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """Host-side: a problem whose workspace exceeds the fixed scratch array is
+    rejected before any HIP call; an invalid shape is named as such."""
+    sh = shape(B=1, T=10_000_000, Hq=16, Hv=32)
+    st = lib.gdn_prefill_chunked_noalloc(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 0, FAKE, 64,
+                                         ctypes.c_void_p(0x900000), NULL, NULL)
+    assert st == gdn.GDN_ERR_UNSUPPORTED and "scratch" in last(lib)
+    st = lib.gdn_prefill_chunked_noalloc(ctypes.byref(shape(Hv=5)), FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL, 64,
+                                         ctypes.c_void_p(0x900000), NULL, NULL)
+    assert st == gdn.GDN_ERR_INVALID_ARG and "multiple" in last(lib)
