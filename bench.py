@@ -21,8 +21,11 @@ stream, gives the per-kernel durations (roofline, breakdown); those event pairs
 cost ~2-3 us per launch boundary, so they are kept off the first pass.
 
 Those pairs add ~2 us to a short launch, so the breakdown's decode, replay and
-snapshot times come from back-to-back loops over every state set between one
-event pair (the per-launch figures are kept beside them as us_event_pairs).
+snapshot times come from back-to-back loops through the C ABI (arguments
+marshalled beforehand, so the host outruns the GPU) over every state set between
+one event pair; medians over 120 calls of one event pair each are reported
+beside them, with the inactive-capture call (zero fill) and the fp16 Qwen-like
+2048-token prefill.
 The breakdown also times, outside the step, the prefix-reuse batch: 16 rows x
 256 bf16 tokens continuing from one broadcast snapshot of a 4096-token prefix
 (event-timed loop over two distinct resident batches), without and with the
@@ -33,6 +36,7 @@ the calibration of the HBM traffic counters.  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -132,9 +136,47 @@ def committed_traffic(kernel):
 # ----------------------------------------------------------------------------- #
 # CPU baseline: the fp64 oracle on a bounded sample of the same step
 # ----------------------------------------------------------------------------- #
-def cpu_baseline(pre, dec, budget_s):
+_WORKER_CASE = None
+
+
+def _warm_worker(_):
+    """Worker start-up (untimed): imports and the workload's inputs, drawn from
+    the same seeded generator as the GPU's, so nothing large crosses processes."""
+    global _WORKER_CASE
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    import gdn_inputs
+    import oracle  # noqa: F401
+    if _WORKER_CASE is None:
+        _WORKER_CASE = gdn_inputs.make("long_varlen")
+    return 0
+
+
+def _oracle_head(h):
+    """One (all sequences, value head h) unit of the packed prefill on the fp64
+    oracle, in a worker process; returns its wall time."""
     import oracle
-    threads = 1
+    c = _WORKER_CASE
+    t = time.perf_counter()
+    oracle.recurrent(c["q"], c["k"], c["v"], c["g"], c["beta"], c["scale"], c["Hq"], c["Hv"],
+                     cu_seqlens=c["cu_seqlens"], initial_state=c["s0"], heads=[h])
+    return time.perf_counter() - t
+
+
+def _box_cpus():
+    """Cores this process may use, capped at the GPU machine's CPU share of 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(pre, dec, budget_s):
+    """The fp64 oracle on the host, on a bounded sample of the same step: one
+    core (decode stage + as many prefill value heads as the budget allows),
+    then all cores (one worker process per core, one value head each)."""
+    import multiprocessing as mp
+    import oracle
     t0 = time.perf_counter()
     od = oracle.recurrent(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], dec["scale"], dec["Hq"], dec["Hv"],
                           cu_seqlens=dec["cu_seqlens"], initial_state=dec["s0"])
@@ -143,7 +185,7 @@ def cpu_baseline(pre, dec, budget_s):
     n = [min(max(int(c), 0), dec["capacity"], L) for c, L in zip(dec["capture_count"].tolist(), dec["lengths"])]
     oracle.replay(dec["s0"], buf, n, dec["Hq"], dec["Hv"], dec["dk"], dec["dv"], dec["capacity"])
     t_dec = time.perf_counter() - t0
-    # prefill: whole packed workload, a subset of value heads (each head is independent)
+    # prefill on one core: whole packed workload, a subset of value heads (each head is independent)
     heads, t_pre = [], 0.0
     order = [0, 31, 8, 23, 16, 5, 27, 12, 19, 2, 29, 10, 21, 14, 25, 6]
     for h in order:
@@ -156,12 +198,43 @@ def cpu_baseline(pre, dec, budget_s):
             break
     est_step = t_pre * pre["Hv"] / len(heads) + t_dec
     tokens = pre["T"] + dec["T"]
-    return {"value": tokens / est_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, single thread: the full decode+capture+replay stage "
-                       f"({t_dec:.2f} s) and the full {pre['T']}-token prefill for {len(heads)} of "
-                       f"{pre['Hv']} value heads ({t_pre:.2f} s), scaled to all heads; "
-                       f"est. {est_step:.1f} s per step"),
-            "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+    one = {"value": tokens / est_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": (f"fp64 numpy oracle, single thread: the full decode+capture+replay stage "
+                      f"({t_dec:.2f} s) and the full {pre['T']}-token prefill for {len(heads)} of "
+                      f"{pre['Hv']} value heads ({t_pre:.2f} s), scaled to all heads; "
+                      f"est. {est_step:.1f} s per step")}
+    # all cores: one worker process per core, each running one value head of the
+    # whole packed prefill (fresh interpreters, BLAS/OpenMP pinned to one thread)
+    W = _box_cpus()
+    units = [h % pre["Hv"] for h in range(W)]
+    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in env_keys}
+    for k in env_keys:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(W) as pool:
+            pool.map(_warm_worker, range(W), chunksize=1)   # start-up, imports, inputs: untimed
+            t2 = time.perf_counter()
+            per_unit = pool.map(_oracle_head, units, chunksize=1)
+            wall = time.perf_counter() - t2
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    est_all = wall * pre["Hv"] / len(units) + t_dec / W
+    all_cores = {"value": tokens / est_all, "unit": "tokens/s", "cores": W, "kind": "oracle",
+                 "sample": (f"fp64 numpy oracle, {W} worker processes of one thread: {len(units)} value heads of "
+                            f"the full {pre['T']}-token prefill at once ({wall:.2f} s wall, "
+                            f"{sum(per_unit) / len(per_unit):.2f} s per head), scaled to all {pre['Hv']} heads, "
+                            f"plus the decode stage split over the workers; est. {est_all:.2f} s per step")}
+    out = dict(all_cores)
+    out["one_core"] = one
+    out["cpu"] = platform.processor() or platform.machine()
+    out["host_cpus"] = os.cpu_count()
+    return out
 
 
 # ----------------------------------------------------------------------------- #
@@ -214,6 +287,64 @@ def _prefix_batch(gdn, gi, dev, C, iters):
     gdn.gdn_profile_enable(False)
     res["kernels_no_finals"] = {k: {"avg_us": 1000.0 * ms / n} for k, (n, ms) in gdn.gdn_profile_collect().items()}
     return res
+
+
+MEDIAN_CALLS = 120
+
+
+def loop_us(fn, n):
+    """Mean time per call of n calls back to back (one event pair)."""
+    import torch
+    for i in range(4):
+        fn(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / n
+
+
+def median_call_us(fn, n, warm=10):
+    """Median over n calls of one event pair per call (after warm-ups)."""
+    import statistics
+    import torch
+    for i in range(warm):
+        fn(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(warm + i)
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median(1000.0 * a.elapsed_time(b) for a, b in ev)
+
+
+def _qwen_prefill(gdn, gi, dev, torch):
+    """The fp16 Qwen-like prefill (1 sequence of 2048 tokens, Hq=2, Hv=6,
+    dk=dv=128, chunk 64, random initial state): median call time over
+    MEDIAN_CALLS calls, tokens/s and the fraction of the fp16 MFMA peak."""
+    c = gi.make("qwen_fp16")
+    p = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in c.items()}
+    args = [p[x][None] for x in ("q", "k", "v", "g", "beta")]
+    o = torch.empty_like(args[2])
+    fin = torch.empty((1, c["Hv"], c["dk"], c["dv"]), device=dev)
+    sh = gdn.gdn_shape(1, c["T"], c["Hq"], c["Hv"], c["dk"], c["dv"], c["scale"], gdn.GDN_F16)
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(sh, c["chunk"], False), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        gdn.gdn_prefill_chunked(*args, scale=c["scale"], initial_state=p["s0"], chunk_size=c["chunk"], o=o,
+                                final_state=fin, workspace=ws)
+    us = median_call_us(call, MEDIAN_CALLS)
+    F = prefill_flops([c["T"]], c["chunk"], c["Hq"], c["Hv"], c["dk"], c["dv"])
+    return {"workload": "fp16 prefill, 1 sequence x 2048 tokens, Hq=2, Hv=6, dk=dv=128, chunk 64, random initial "
+                        "state, final state written", "us_median": us, "tokens_per_s": c["T"] / (us * 1e-6),
+            "algorithmic_gflop": F / 1e9, "tflops": F / (us * 1e-6) / 1e12,
+            "mfma_frac": F / (us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+            "note": "latency bound: 32 chunks in sequence over 6 value heads (24 workgroups)"}
 
 
 def main():
@@ -311,29 +442,52 @@ def main():
     # 4096-token prefix, without and with the rows' final states.
     batch = _prefix_batch(gdn, gi, dev, C, args.steps)
 
-    # Timed region 4 (breakdown): the short launches back to back, one event pair
-    # around a loop over every state set (each call's state is cold), so their
-    # per-call times carry no per-launch event cost.
-    def loop_us(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return 1000.0 * e0.elapsed_time(e1) / n
+    # Timed region 4 (breakdown): the short launches through the C ABI with
+    # their arguments marshalled beforehand, so the host issues them faster than
+    # the GPU runs them: (a) back to back, one event pair around a loop over
+    # every state set (each call's state cold); (b) one event pair per call over
+    # MEDIAN_CALLS calls after 10 warm-ups, median reported.
+    lib = gdn.load_library()
+    vp = ctypes.c_void_p
+    P = lambda t: vp(t.data_ptr())
+    stream = vp(torch.cuda.current_stream(dev).cuda_stream)
+    dsh = gdn.gdn_shape(B, dec["T"], Hq, Hv, dk, dv, dec["scale"], gdn.GDN_BF16)
+    dargs = [(ctypes.byref(dsh), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(states[j]),
+              Hv * dk * dv, P(d["cu_seqlens"]), P(dec_o), P(finals[j])) for j in range(STATE_SETS)]
+    cnt_p, su_p, acc_p = P(counts), P(su), P(accept)
 
-    def dec_call(i):
-        gdn.gdn_recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"],
-                               initial_state=states[i % STATE_SETS], cu_seqlens=d["cu_seqlens"], o=dec_o,
-                               final_state=finals[i % STATE_SETS], state_update_capacity=cap,
-                               capture_count=counts, state_update_active=1, state_update=su)
+    def dec_call(i, active=1):
+        st = lib.gdn_recurrent_step(*dargs[i % STATE_SETS], cap, cnt_p, active, su_p, stream)
+        assert st == 0, st
+
+    def rep_call(i):
+        st = lib.gdn_replay_state_updates(B, Hq, Hv, dk, dv, cap, su_p, acc_p, P(states[i % STATE_SETS]), stream)
+        assert st == 0, st
+
+    snap_args = [(P(fins[j]), P(snaps[j]), N, Hv, dk, dv, stream) for j in range(2)]
+
+    def snap_call(i):
+        assert lib.gdn_state_snapshot(*snap_args[i % 2]) == 0
 
     loop = {"decode": loop_us(dec_call, 2 * STATE_SETS),
-            "replay": loop_us(lambda i: gdn.gdn_replay_state_updates(states[i % STATE_SETS], su, accept, Hq=Hq),
-                              2 * STATE_SETS),
-            "snapshot": loop_us(lambda i: gdn.gdn_state_snapshot(fins[i % 2], snaps[i % 2]), 2 * STATE_SETS)}
+            "decode_inactive": loop_us(lambda i: dec_call(i, 0), 2 * STATE_SETS),
+            "replay": loop_us(rep_call, 2 * STATE_SETS),
+            "snapshot": loop_us(snap_call, 2 * STATE_SETS)}
+    med = {"decode": median_call_us(dec_call, MEDIAN_CALLS), "decode_inactive": median_call_us(lambda i: dec_call(i, 0), MEDIAN_CALLS),
+           "replay": median_call_us(rep_call, MEDIAN_CALLS), "snapshot": median_call_us(snap_call, MEDIAN_CALLS)}
+    # the replays above keep applying records to the rotating state sets; they
+    # only serve timing (values grow but stay finite over these few calls)
+
+    # Timed region 5 (breakdown): the two prefill workloads, median over
+    # MEDIAN_CALLS calls of one event pair each: the step's packed prefill and
+    # the fp16 Qwen-like single sequence (2048 tokens, Hq=2, Hv=6).
+    def pre_call(i):
+        p = pre_sets[i % 2]
+        gdn.gdn_prefill_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], scale=p["scale"],
+                                initial_state=p["s0"], cu_seqlens=p["cu_seqlens"], chunk_size=C,
+                                o=outs[i % 2], final_state=fins[i % 2], workspace=ws)
+    med["prefill"] = median_call_us(pre_call, MEDIAN_CALLS)
+    qwen = _qwen_prefill(gdn, gi, dev, torch)
 
     # Untimed: one plain copy of a cold 256 MiB buffer (the largest copy_kernel
     # dispatch of the command), whose FETCH_SIZE / WRITE_SIZE readings calibrate
@@ -357,24 +511,37 @@ def main():
     ev_us = {k: per_step_us.get(n, float("nan")) for k, n in (("decode", "recurrent_step_kernel"),
                                                               ("replay", "replay_kernel"),
                                                               ("snapshot", "copy_kernel"))}
+    R = Hv + Hq * dk + Hv * dv
+    dbytes_inactive = dbytes - sum(n_cap) * R * 4 + B * cap * R * 4   # no records, the whole buffer zeroed
 
     breakdown = {
-        "prefill": {"us": t_prefill_us, "tokens_per_s": pre["T"] / (t_prefill_us * 1e-6),
+        "prefill": {"us": t_prefill_us, "us_median": med["prefill"], "median_calls": MEDIAN_CALLS,
+                    "tokens_per_s": pre["T"] / (t_prefill_us * 1e-6),
                     "algorithmic_gflop": F / 1e9, "tflops": F / (t_prefill_us * 1e-6) / 1e12,
                     "mfma_frac": F / (t_prefill_us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+                    "mfma_frac_median": F / (med["prefill"] * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
                     "algorithmic_mb": pbytes / 1e6,
                     "hbm_frac": pbytes / (t_prefill_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
-        "decode": {"us": t_dec_us, "us_event_pairs": ev_us["decode"], "tokens": dec["T"],
+        "decode": {"us": t_dec_us, "us_median": med["decode"], "us_event_pairs": ev_us["decode"], "tokens": dec["T"],
                    "algorithmic_mb": dbytes / 1e6,
                    "gbs": dbytes / (t_dec_us * 1e-6) / 1e9,
                    "hbm_frac": dbytes / (t_dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
-        "replay": {"us": t_rep_us, "us_event_pairs": ev_us["replay"], "records": sum(n_cap),
-                   "algorithmic_mb": rbytes / 1e6,
+        "decode_inactive_capture": {"us": loop["decode_inactive"], "us_median": med["decode_inactive"],
+                                    "note": "state_update_active=0: zero-fill of the whole capture buffer + the step",
+                                    "algorithmic_mb": dbytes_inactive / 1e6,
+                                    "gbs": dbytes_inactive / (loop["decode_inactive"] * 1e-6) / 1e9,
+                                    "hbm_frac": dbytes_inactive / (loop["decode_inactive"] * 1e-6) / 1e9 / PEAK_HBM_GBS},
+        "replay": {"us": t_rep_us, "us_median": med["replay"], "us_event_pairs": ev_us["replay"],
+                   "records": sum(n_cap), "algorithmic_mb": rbytes / 1e6,
                    "gbs": rbytes / (t_rep_us * 1e-6) / 1e9,
                    "hbm_frac": rbytes / (t_rep_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
-        "snapshot": {"us": t_snap_us, "us_event_pairs": ev_us["snapshot"],
+        "snapshot": {"us": t_snap_us, "us_median": med["snapshot"], "us_event_pairs": ev_us["snapshot"],
                      "gbs": 2 * N * Hv * dk * dv * 4 / (t_snap_us * 1e-6) / 1e9},
+        "qwen_fp16_prefill": qwen,
         "prefix_batch": batch,
+        "timing": ("us: mean of back-to-back calls through the C ABI over rotating cold state sets (decode, "
+                   "replay, snapshot) or the step's per-kernel event pairs (prefill); us_median: median over "
+                   f"{MEDIAN_CALLS} calls of one event pair each, after 10 warm-ups"),
     }
 
     # dominant kernel: the one with the largest time per step
