@@ -348,10 +348,8 @@ static gdn_status recurrent_impl(const gdn_shape* sh, const gdn_prologue* pro, c
   if (sh->B == 0) return GDN_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cap > 0 && !active) {
-    hipError_t e = gdn::launch_zero_fill(su, su_elems, s);
-    if (e != hipSuccess) return hip_fail(e, "state_update zero fill");
-  }
+  // state_update_active = 0: the step kernel itself zero-fills the whole
+  // state_update buffer (no separate launch)
   gdn::DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.s0 = s0; a.s0_stride = s0_stride; a.s_out = s_out; a.o = o; a.cu = cu;

@@ -91,13 +91,12 @@ inline size_t chunk_block_bytes(DType dt) {
 
 // Opt-in per-kernel event timing (gdn_profile_enable / gdn_profile_collect).
 enum KernelId : int {
-  K_PLAN = 0, K_PREP, K_STATE, K_RECURRENT, K_ZERO_FILL, K_REPLAY, K_COPY, kNumKernels
+  K_PLAN = 0, K_PREP, K_STATE, K_RECURRENT, K_REPLAY, K_COPY, kNumKernels
 };
 void prof_begin(KernelId id, hipStream_t s);
 void prof_end(KernelId id, hipStream_t s);
 
 hipError_t launch_recurrent(DType dt, const DecodeArgs& a, hipStream_t s);
-hipError_t launch_zero_fill(float* p, size_t n, hipStream_t s);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t s);
 hipError_t launch_copy(const float* src, float* dst, size_t n, hipStream_t s);
 hipError_t launch_prefill(DType dt, const PrefillArgs& a, hipStream_t s);

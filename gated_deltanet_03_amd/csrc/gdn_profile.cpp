@@ -16,8 +16,7 @@ namespace gdn {
 namespace {
 
 const char* const kNames[kNumKernels] = {"chunk_plan_kernel", "chunk_prep_kernel", "chunk_state_kernel",
-                                          "recurrent_step_kernel", "fill_zero_kernel", "replay_kernel",
-                                          "copy_kernel"};
+                                          "recurrent_step_kernel", "replay_kernel", "copy_kernel"};
 
 struct Rec {
   int id;

@@ -1,6 +1,6 @@
-// Recurrent (token-by-token) GDN step with compact state-update capture, the
-// replay of captured updates, and the plain fill / copy kernels used for the
-// inactive-capture zero fill and for state snapshots.
+// Recurrent (token-by-token) GDN step with compact state-update capture (and,
+// when capture is inactive, the zero fill of the capture buffer), the replay
+// of captured updates, and the plain copy kernel used for state snapshots.
 //
 // Method: the gated delta rule, alpha = exp(g), delta = beta (v - alpha S^T k),
 // S <- alpha S + k delta^T, o = scale S^T q (post-update state).  Capture and
@@ -153,6 +153,16 @@ __global__ __launch_bounds__(64 * WPG) void recurrent_step_kernel(DecodeArgs p) 
   constexpr int RPL = DK / 16;
   const int lane = threadIdx.x & 63;
   const int cg = lane & 3, rg = lane >> 2;
+  if (p.cap > 0 && !p.active) {
+    // inactive capture: every thread of the grid zero-fills its share of the
+    // whole state_update buffer [B, cap, R] (16-byte aligned), then runs the
+    // step without writing records
+    const size_t n = (size_t)p.B * p.cap * ((size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * p.dv);
+    const size_t n4 = n / 4, stride = (size_t)gridDim.x * blockDim.x;
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (size_t j = i; j < n4; j += stride) reinterpret_cast<float4*>(p.su)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (size_t j = n4 * 4 + i; j < n; j += stride) p.su[j] = 0.f;
+  }
   int b, h, slice;
   if (!slice_of<WPG>(p.Hv, p.dv / DVS, p.B, b, h, slice)) return;
   const int G = p.Hv / p.Hq;
@@ -399,14 +409,6 @@ __global__ __launch_bounds__(64 * WPG) void replay_kernel(ReplayArgs p) {
   for (int r = 0; r < RPL; ++r) store_state4(st + (size_t)(row0 + r) * dv + col, S[r]);
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
-  const size_t n4 = n / 4;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (size_t j = i; j < n4; j += stride) reinterpret_cast<float4*>(p)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (size_t j = n4 * 4 + i; j < n; j += stride) p[j] = 0.f;
-}
-
 __global__ __launch_bounds__(256) void copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                    size_t n) {
   const size_t n4 = n / 4;
@@ -509,14 +511,6 @@ static unsigned stream_grid(size_t n) {
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
   return (unsigned)blocks;
-}
-
-hipError_t launch_zero_fill(float* p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  prof_begin(K_ZERO_FILL, s);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(stream_grid(n)), dim3(256), 0, s, p, n);
-  prof_end(K_ZERO_FILL, s);
-  return hipGetLastError();
 }
 
 hipError_t launch_copy(const float* src, float* dst, size_t n, hipStream_t s) {
