@@ -671,8 +671,10 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
   // 16-bit inputs with dedicated loaders: the chain fetches A' into its
   // registers and only MP is staged (fp32 A' fragments are too wide for the
   // chain's registers; where the chain waves issue the loads themselves the
-  // staged form measured faster)
-  constexpr bool AREG = ES == 2 && NDW > 0;
+  // staged form measured faster).  The state-emitting variant stages A' too:
+  // its chain waves store every chunk's state, and a wait for register-held A'
+  // would also wait for those stores.
+  constexpr bool AREG = ES == 2 && NDW > 0 && !EMIT;
   constexpr int NA0 = AREG ? NA / 2 : 0;  // first staged piece of the A'/MP region
   extern __shared__ __align__(16) unsigned char smem_raw[];
   unsigned char* fixed = smem_raw + SM::NBUF * SM::STAGE;
@@ -1158,7 +1160,9 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
         next_sb(NST - 1);
         if constexpr (EMIT) {
           // the state after this chunk's last token, in the [dk, dv] state layout:
-          // a wave-uniform row base per store plus one per-lane 32-bit offset
+          // a wave-uniform row base per store plus one per-lane 32-bit offset;
+          // non-temporal, so the stream of states does not evict the K/Q tiles
+          // the other workgroups of the head still read from L2
           if (active && (int64_t)(cbeg + c) < p.chunk_states_cap) {
             float* cs = p.chunk_states + ((size_t)(cbeg + c) * p.Hv + h) * DK * dv;
             const int lo = (DK < 32 ? 4 * g4 : 8 * g4) * dv + col0 + i16;
@@ -1167,7 +1171,7 @@ __global__ __launch_bounds__(64 * (2 * NG + NDW)) void chunk_state_kernel(Prefil
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const int row = perm_dk<DK>(16 * r + q);          // lane group 0's row
-                (cs + (size_t)row * dv)[lo] = S[r][q];
+                __builtin_nontemporal_store(S[r][q], (cs + (size_t)row * dv) + lo);
               }
           }
         }
