@@ -83,6 +83,14 @@ __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d)
 // moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// [a, b) clamped to [0, total], so malformed offsets stay in bounds.
+__device__ __forceinline__ void clamp_range(int a, int b, int32_t total, int& t0, int& t1) {
+  a = a < 0 ? 0 : (a > total ? total : a);
+  b = b < a ? a : (b > total ? total : b);
+  t0 = a;
+  t1 = b;
+}
+
 // Token range of sequence s: dense rows of T tokens when cu == nullptr, else
 // [cu[s], cu[s+1]) clamped to [0, total] so malformed offsets stay in bounds.
 __device__ __forceinline__ void seq_range(const int32_t* __restrict__ cu, int32_t T, int32_t total,
@@ -91,11 +99,7 @@ __device__ __forceinline__ void seq_range(const int32_t* __restrict__ cu, int32_
     t0 = s * T;
     t1 = t0 + T;
   } else {
-    int a = cu[s], b = cu[s + 1];
-    a = a < 0 ? 0 : (a > total ? total : a);
-    b = b < a ? a : (b > total ? total : b);
-    t0 = a;
-    t1 = b;
+    clamp_range(cu[s], cu[s + 1], total, t0, t1);
   }
 }
 

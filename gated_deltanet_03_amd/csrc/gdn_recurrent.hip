@@ -133,19 +133,41 @@ struct TokenIn {
   float g, beta;
 };
 
-// Workgroup id and wave -> (row, value head, column slice): workgroups of WPG
-// waves, each wave one slice; the nsl / WPG workgroups of one (row, head) get
-// ids congruent mod 8 (one XCD).  False for padding workgroups.
-template <int WPG>
-__device__ __forceinline__ bool slice_of(int Hv, int nsl, int B, int& b, int& h, int& slice) {
-  const int ngr = nsl / WPG;
+// Workgroup id and wave -> (row, value head, column slice, row part):
+// workgroups of NWR * SPG waves, SPG adjacent column slices of one (row, head)
+// state, each slice served by NWR waves that split its dk rows.  The
+// workgroups of one state get ids congruent mod 8 (one XCD).  False for
+// padding workgroups.
+template <int NWR, int SPG>
+__device__ __forceinline__ bool slice_of(int Hv, int nsl, int B, int& b, int& h, int& slice, int& wr) {
+  const int ngr = nsl / SPG;
   const int xcd = (int)(blockIdx.x & 7), rnd = (int)(blockIdx.x >> 3);
   const int grp = (rnd / ngr) * 8 + xcd;
   if (grp >= B * Hv) return false;
-  slice = (rnd % ngr) * WPG + (int)(threadIdx.x >> 6);
+  const int wi = (int)(threadIdx.x >> 6);
+  slice = (rnd % ngr) * SPG + wi / NWR;
+  wr = wi % NWR;
   b = grp / Hv;
   h = grp % Hv;
   return true;
+}
+
+__device__ const int32_t kZeroWords[4] = {0, 0, 0, 0};
+__device__ const float kZeroFloats[4] = {0.f, 0.f, 0.f, 0.f};
+
+// Read-only wave-uniform value through the constant address space, so it is
+// fetched with a scalar load (counted apart from the vector loads in flight).
+template <typename X>
+__device__ __forceinline__ X load_uniform(const X* ptr) {
+  return *(const __attribute__((address_space(4))) X*)ptr;
+}
+
+__device__ __forceinline__ void zero_fill_records(const DecodeArgs& p, int dk) {
+  const size_t n = (size_t)p.B * p.cap * ((size_t)p.Hv + (size_t)p.Hq * dk + (size_t)p.Hv * p.dv);
+  const size_t n4 = n / 4, stride = (size_t)gridDim.x * blockDim.x;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (size_t j = i; j < n4; j += stride) reinterpret_cast<float4*>(p.su)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (size_t j = n4 * 4 + i; j < n; j += stride) p.su[j] = 0.f;
 }
 
 template <typename T, int DK, int WPG>
@@ -153,50 +175,35 @@ __global__ __launch_bounds__(64 * WPG) void recurrent_step_kernel(DecodeArgs p) 
   constexpr int RPL = DK / 16;
   const int lane = threadIdx.x & 63;
   const int cg = lane & 3, rg = lane >> 2;
-  if (p.cap > 0 && !p.active) {
-    // inactive capture: every thread of the grid zero-fills its share of the
-    // whole state_update buffer [B, cap, R] (16-byte aligned), then runs the
-    // step without writing records
-    const size_t n = (size_t)p.B * p.cap * ((size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * p.dv);
-    const size_t n4 = n / 4, stride = (size_t)gridDim.x * blockDim.x;
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (size_t j = i; j < n4; j += stride) reinterpret_cast<float4*>(p.su)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (size_t j = n4 * 4 + i; j < n; j += stride) p.su[j] = 0.f;
+  // inactive capture: every thread of the grid zero-fills its share of the
+  // whole state_update buffer [B, cap, R] (16-byte aligned) after its step,
+  // which writes no records; placed after every load of the kernel so that
+  // the compiler may fetch the row's wave-uniform values with scalar loads
+  const bool fill = p.cap > 0 && !p.active;
+  int b, h, slice, wr;
+  if (!slice_of<1, WPG>(p.Hv, p.dv / DVS, p.B, b, h, slice, wr)) {
+    if (fill) zero_fill_records(p, DK);
+    return;
   }
-  int b, h, slice;
-  if (!slice_of<WPG>(p.Hv, p.dv / DVS, p.B, b, h, slice)) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  h = __builtin_amdgcn_readfirstlane(h);
+  slice = __builtin_amdgcn_readfirstlane(slice);
   const int G = p.Hv / p.Hq;
   const int hk = h / G;
   const int dv = p.dv;
   const int col = slice * DVS + cg * 4;
   const int row0 = rg * RPL;
 
-  int t0, t1;
-  seq_range(p.cu, p.T, p.total, b, t0, t1);
-
-  const T* __restrict__ qp = static_cast<const T*>(p.q);
-  const T* __restrict__ kp = static_cast<const T*>(p.k);
-  const T* __restrict__ vp = static_cast<const T*>(p.v);
-  T* __restrict__ op = static_cast<T*>(p.o);
-
-  // gate prologue constants of this head: g = -exp(A_log) softplus(g_in + dt_bias)
-  const bool gate = p.pro.A_log != nullptr;
-  const float negA = gate ? -expf(p.pro.A_log[h]) : 0.f;
-  const float dtb = gate && p.pro.dt_bias != nullptr ? p.pro.dt_bias[h] : 0.f;
-
-  auto load_tok = [&](int t, TokenIn<T, RPL>& in) {
-    const size_t qk = ((size_t)t * p.Hq + hk) * DK + row0;
-    in.k.load(kp + qk);
-    in.q.load(qp + qk);
-    in.v.load(vp + ((size_t)t * p.Hv + h) * dv + col);
-    in.g = p.g[(size_t)t * p.Hv + h];
-    in.beta = p.beta[(size_t)t * p.Hv + h];
-  };
-
-  TokenIn<T, RPL> ring[NPF];
-#pragma unroll
-  for (int u = 0; u < NPF; ++u)
-    if (t0 + u < t1) load_tok(t0 + u, ring[u]);
+  // The row's wave-uniform data: scalar loads issued before the state loads,
+  // unconditionally (absent arrays read zeros), so that nothing waits for them
+  // before the state is requested.
+  const bool capture = p.cap > 0 && p.active;
+  const bool gate = p.pro.A_log != nullptr;   // g = -exp(A_log) softplus(g_in + dt_bias)
+  const int cu0 = load_uniform(p.cu != nullptr ? p.cu + b : kZeroWords);
+  const int cu1 = load_uniform(p.cu != nullptr ? p.cu + b + 1 : kZeroWords);
+  const int cnt = load_uniform(capture ? p.counts + b : kZeroWords);
+  const float alog = load_uniform(gate ? p.pro.A_log + h : kZeroFloats);
+  const float dtb = load_uniform(gate && p.pro.dt_bias != nullptr ? p.pro.dt_bias + h : kZeroFloats);
 
   // State slice: rows row0..row0+RPL-1, columns col..col+3.
   float4 S[RPL];
@@ -210,11 +217,39 @@ __global__ __launch_bounds__(64 * WPG) void recurrent_step_kernel(DecodeArgs p) 
     for (int r = 0; r < RPL; ++r) S[r] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
+  int t0, t1;
+  if (p.cu == nullptr) {
+    t0 = b * p.T;
+    t1 = t0 + p.T;
+  } else {
+    clamp_range(cu0, cu1, p.total, t0, t1);
+  }
+
+  const T* __restrict__ qp = static_cast<const T*>(p.q);
+  const T* __restrict__ kp = static_cast<const T*>(p.k);
+  const T* __restrict__ vp = static_cast<const T*>(p.v);
+  T* __restrict__ op = static_cast<T*>(p.o);
+
+  const float negA = gate ? -expf(alog) : 0.f;
+
+  auto load_tok = [&](int t, TokenIn<T, RPL>& in) {
+    const size_t qk = ((size_t)t * p.Hq + hk) * DK + row0;
+    in.k.load(kp + qk);
+    in.q.load(qp + qk);
+    in.v.load(vp + ((size_t)t * p.Hv + h) * dv + col);
+    in.g = load_uniform(p.g + (size_t)t * p.Hv + h);
+    in.beta = load_uniform(p.beta + (size_t)t * p.Hv + h);
+  };
+
+  TokenIn<T, RPL> ring[NPF];
+#pragma unroll
+  for (int u = 0; u < NPF; ++u)
+    if (t0 + u < t1) load_tok(t0 + u, ring[u]);
+
   int ncap = 0;
-  if (p.cap > 0 && p.active) {
-    int c = p.counts[b];
-    int lim = p.cap < (t1 - t0) ? p.cap : (t1 - t0);
-    ncap = c < 0 ? 0 : (c > lim ? lim : c);
+  if (capture) {
+    const int lim = p.cap < (t1 - t0) ? p.cap : (t1 - t0);
+    ncap = cnt < 0 ? 0 : (cnt > lim ? lim : cnt);
   }
   const size_t R = (size_t)p.Hv + (size_t)p.Hq * DK + (size_t)p.Hv * dv;
   const bool write_key = (h % G == 0) && slice == 0 && cg == 0;
@@ -325,29 +360,36 @@ __global__ __launch_bounds__(64 * WPG) void recurrent_step_kernel(DecodeArgs p) 
     for (int r = 0; r < RPL; ++r)
       store_state4(so + (size_t)(row0 + r) * dv + col, S[r]);
   }
+  if (fill) zero_fill_records(p, DK);
 }
 
 // Replay of captured records.  Records are fetched in batches (all of a
 // batch's loads issued before its first record is applied) since each
-// application is only two VALU operations per state element.  Same slice
-// geometry as the recurrent step.  VEC: every record field this lane reads
-// starts on a 16-byte boundary (the record buffer is 16-byte aligned and Hv and
-// R are multiples of 4), so keys and deltas are read as float4.
+// application is only two VALU operations per state element.  Geometry: column
+// slices of CW columns, each split over NWR waves by dk rows (no reduction
+// couples rows here); lane = rg * (CW / 4) + cg, cg a float4 of columns, rg a
+// group of RPL adjacent rows.  With CW = 32 every wave load or store
+// instruction moves whole 128-byte state lines.  VEC: every record field this
+// lane reads starts on a 16-byte boundary (the record buffer is 16-byte aligned
+// and Hv and R are multiples of 4), so keys and deltas are read as float4.
+#ifndef REPLAY_SPG
+#define REPLAY_SPG 2
+#endif
 constexpr int RB = 4;   // records per full batch; a tail of 2 and 1 follows
 
-template <int DK, bool VEC, int WPG>
-__global__ __launch_bounds__(64 * WPG) void replay_kernel(ReplayArgs p) {
-  constexpr int RPL = DK / 16;
+template <int DK, bool VEC, int CW, int NWR, int SPG>
+__global__ __launch_bounds__(64 * NWR * SPG) void replay_kernel(ReplayArgs p) {
+  constexpr int CPL = CW / 4, RG = 64 / CPL, RPL = DK / (NWR * RG);
+  static_assert(RPL >= 1, "more row groups than rows");
   static_assert(!VEC || RPL % 4 == 0, "vector key reads need 4 rows per lane");
   const int lane = threadIdx.x & 63;
-  const int cg = lane & 3, rg = lane >> 2;
-  int b, h, slice;
-  if (!slice_of<WPG>(p.Hv, p.dv / DVS, p.B, b, h, slice)) return;
+  const int cg = lane % CPL, rg = lane / CPL;
+  int b, h, slice, wr;
+  if (!slice_of<NWR, SPG>(p.Hv, p.dv / CW, p.B, b, h, slice, wr)) return;
   const int hk = h / (p.Hv / p.Hq);
   const int dv = p.dv;
-  const int col = slice * DVS + cg * 4;
-  const int row0 = rg * RPL;
-
+  const int col = slice * CW + cg * 4;
+  const int row0 = wr * (DK / NWR) + rg * RPL;
   int m = p.counts[b];
   m = m < 0 ? 0 : (m > p.cap ? p.cap : m);
   if (m == 0) return;
@@ -422,11 +464,11 @@ __global__ __launch_bounds__(256) void copy_kernel(const float* __restrict__ src
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-// Padded 1-D grid for the XCD-aware slice order: 8 * (dv / 16 / WPG) *
-// ceil(B*Hv / 8) workgroups of WPG waves.
-static unsigned slice_grid(int B, int Hv, int dv, int wpg) {
+// Padded 1-D grid for the XCD-aware slice order: 8 * (dv / cw / spg) *
+// ceil(B*Hv / 8) workgroups, each of spg column slices of cw columns.
+static unsigned slice_grid(int B, int Hv, int dv, int cw, int spg) {
   const long long groups = (long long)B * Hv;
-  return (unsigned)(8LL * (dv / DVS / wpg) * ((groups + 7) / 8));
+  return (unsigned)(8LL * (dv / cw / spg) * ((groups + 7) / 8));
 }
 
 // Waves per workgroup of the recurrent step: the state's slices in groups of
@@ -436,8 +478,8 @@ static int slices_per_group(int dv) { return dv / DVS >= 4 ? 4 : dv / DVS; }
 template <typename T, int DK, int WPG>
 static hipError_t launch_rec_w(const DecodeArgs& a, hipStream_t s) {
   prof_begin(K_RECURRENT, s);
-  hipLaunchKernelGGL((recurrent_step_kernel<T, DK, WPG>), dim3(slice_grid(a.B, a.Hv, a.dv, WPG)), dim3(64 * WPG), 0, s,
-                     a);
+  hipLaunchKernelGGL((recurrent_step_kernel<T, DK, WPG>), dim3(slice_grid(a.B, a.Hv, a.dv, DVS, WPG)),
+                     dim3(64 * WPG), 0, s, a);
   prof_end(K_RECURRENT, s);
   return hipGetLastError();
 }
@@ -472,17 +514,24 @@ hipError_t launch_recurrent(DType dt, const DecodeArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int DK, bool VEC, int WPG>
+template <int DK, bool VEC, int CW, int NWR, int SPG>
 static hipError_t launch_replay_w(const ReplayArgs& a, hipStream_t s) {
   prof_begin(K_REPLAY, s);
-  hipLaunchKernelGGL((replay_kernel<DK, VEC, WPG>), dim3(slice_grid(a.B, a.Hv, a.dv, WPG)), dim3(64 * WPG), 0, s, a);
+  hipLaunchKernelGGL((replay_kernel<DK, VEC, CW, NWR, SPG>), dim3(slice_grid(a.B, a.Hv, a.dv, CW, SPG)),
+                     dim3(64 * NWR * SPG), 0, s, a);
   prof_end(K_REPLAY, s);
   return hipGetLastError();
 }
 
+// 32-column slices over two waves each (whole 128-byte lines per instruction);
+// dv = 16 keeps one wave per 16-column slice.
 template <int DK, bool VEC>
 static hipError_t launch_replay_v(const ReplayArgs& a, hipStream_t s) {
-  return launch_replay_w<DK, VEC, 1>(a, s);
+  if (a.dv % 32 == 0) {
+    if (REPLAY_SPG >= 2 && a.dv >= 64) return launch_replay_w<DK, VEC, 32, 2, REPLAY_SPG>(a, s);
+    return launch_replay_w<DK, VEC, 32, 2, 1>(a, s);
+  }
+  return launch_replay_w<DK, VEC, 16, 1, 1>(a, s);
 }
 
 template <int DK>
