@@ -56,21 +56,22 @@ def test_repeated_calls_are_bitwise_identical(gdn):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_rows_do_not_depend_on_the_geometry(gdn, dtype):
+@pytest.mark.parametrize("C", [32, 64])
+def test_rows_do_not_depend_on_the_geometry(gdn, dtype, C):
     lengths = [150, 64, 3, 97]
     Hq, Hv = 2, 4
     case = gi.random_case(9700, lengths, Hq=Hq, Hv=Hv, dk=128, dv=128, dtype=dtype)
     # 4 rows x 4 heads x 4 slices = 64 items: the 32-column geometry; 40 extra
     # rows make 704 items > 2 per CU: the 64-column geometry
     filler = gi.random_case(9701, [80] * 40, Hq=Hq, Hv=Hv, dk=128, dv=128, dtype=dtype)
-    say(f"case geometry independence {dtype} lengths={lengths} + 40 x 80")
+    say(f"case geometry independence {dtype} C={C} lengths={lengths} + 40 x 80")
     small = to_dev(case)
     big = to_dev({k: (torch.cat([case[k], filler[k]]) if k in ("q", "k", "v", "g", "beta", "s0") else case[k])
                   for k in case})
     cu = torch.tensor([0] + list(torch.cumsum(torch.tensor(lengths + [80] * 40), 0)), dtype=torch.int32)
     big["cu_seqlens"] = cu.to(small["q"].device)
-    o1, f1 = run(gdn, small, case["scale"], 64)
-    o2, f2 = run(gdn, big, case["scale"], 64)
+    o1, f1 = run(gdn, small, case["scale"], C)
+    o2, f2 = run(gdn, big, case["scale"], C)
     T = sum(lengths)
     assert torch.equal(o1, o2[:T]), "outputs differ between the two geometries"
     assert torch.equal(f1, f2[:len(lengths)]), "final states differ between the two geometries"
