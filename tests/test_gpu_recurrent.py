@@ -209,3 +209,27 @@ def test_recurrent_in_place_state_and_broadcast(gdn):
                                          cu_seqlens=d["cu_seqlens"])
     torch.cuda.synchronize()
     assert torch.equal(o3, o4) and torch.equal(fin3, fin4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_rows_match_oracle_and_chunked_prefill(gdn, dtype):
+    # rows of many tokens (the 4-deep token ring wraps dozens of times): the
+    # recurrent step against the oracle, and against the chunked prefill of the
+    # same input (the pages' chunked-equals-recurrent invariant)
+    lengths = [130, 64, 1, 97]
+    case = gi.random_case(4242, lengths, Hq=2, Hv=4, dk=128, dv=128, dtype=dtype)
+    say(f"case long recurrent rows {dtype} lengths={lengths}")
+    o, fin, _ = run_step(gdn, case)
+    ref = oracle_run(case)
+    bounds = case_bounds(case)
+    assert_close(o, ref["o"], dtype, "o", bounds=bounds)
+    assert_close(fin, ref["final"], dtype, "final")
+    d = to_dev(case)
+    oc, fc = gdn.gdn_prefill_chunked(*[d[x] for x in ("q", "k", "v", "g", "beta")], scale=case["scale"],
+                                     initial_state=d["s0"], cu_seqlens=d["cu_seqlens"], chunk_size=64)
+    torch.cuda.synchronize()
+    assert_close(oc, ref["o"], dtype, "chunked o", bounds=bounds, chunk=64)
+    assert_close(fc, ref["final"], dtype, "chunked final")
+    if dtype != "f32":   # fp32: both within max-abs 1e-4 of the oracle above
+        assert_close(oc, o.float(), dtype, "chunked vs recurrent o", bounds=bounds, chunk=64)
+        assert_close(fc, fin, dtype, "chunked vs recurrent final")
