@@ -163,7 +163,7 @@ def _oracle_head(h):
 
 
 def _box_cpus():
-    """Cores this process may use, capped at the GPU machine's CPU share of 16."""
+    """Cores this process may use, capped at 16 (the host cores that go with one GPU)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -350,7 +350,7 @@ def _qwen_prefill(gdn, gi, dev, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU (no multi-GPU path); --gpus must be 1",
                           "requested_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -55,7 +55,7 @@ def record_width(Hq: int, Hv: int, dk: int, dv: int) -> int:
     """Floats per capture record: [decay Hv | key Hq*dk | delta Hv*dv].
 
     [PR 32767, "Changes"]: one packed float32 output holds decay, shared-key
-    and delta factors; the packing order is this build's convention.
+    and delta factors; the packing order is this library's convention.
     """
     return Hv + Hq * dk + Hv * dv
 
@@ -185,7 +185,7 @@ def capture(k, alpha, delta, Hq, Hv, capacity, capture_count, active,
 
     [PR 32767, "Changes"]: for each row b the first n_b tokens are captured,
     n_b = min(max(capture_count[b], 0), capacity, L_b) (the clamp bounds are
-    this build's reading).  Record c of row b holds, for token start_b + c:
+    the reading this library takes).  Record c of row b holds, for token start_b + c:
     decay[h] = alpha, key[hk] = k (fp32, stored once per key head), delta[h].
     With ``active == 0`` the whole buffer is zero and every entry is specified;
     when active, uncaptured entries are unspecified (mask False).
