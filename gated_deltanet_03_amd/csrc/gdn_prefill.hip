@@ -557,7 +557,7 @@ __global__ __launch_bounds__(64, (sizeof(T) == 4 && DK == 128) ? 1 : ((HPW == 1 
 
 // ---------------------------------------------------------------------------
 // 3. state pass: one workgroup per (sequence, value head, slice of 16*NG columns),
-//    2*NG compute waves (NG = 2 or 4 column groups of 16) plus NDW load-issuing
+//    2*NG compute waves (NG = 1, 2 or 4 column groups of 16) plus NDW load-issuing
 //    waves.
 //
 //    Each 16-column group of the slice is served by two waves: a chain wave

@@ -21,10 +21,13 @@
 // workgroup of the recurrent step holds WPG waves, the adjacent column slices
 // of one (row, head) state (up to 4 of its dv / 16 slices), so the two
 // 64-byte halves of every 128-byte state line are requested from one CU at
-// about the same time (34-token decode: 12.8 us instead of 13.9 us per call;
-// replay keeps one slice per workgroup, which measured faster for it).
-// Workgroups of one state get ids that agree mod 8, so they run on one XCD.
-// The state is read once and written once per call.
+// about the same time (34-token decode: 12.8 us instead of 13.9 us per call).
+// The replay, which needs no dk-reduction, uses 32-column slices split over
+// two waves by rows instead (whole 128-byte lines per instruction).  Each
+// row's wave-uniform values (token range, capture count, gates, per-token g
+// and beta) come through scalar loads.  Workgroups of one state get ids that
+// agree mod 8, so they run on one XCD.  The state is read once and written
+// once per call.
 #include <type_traits>
 
 #include "gdn_device.h"
